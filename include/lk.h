@@ -1,0 +1,163 @@
+/*
+ * lk.h -- C ABI of the MI355X (gfx950) lightning-indexer hot path.
+ *
+ * The indexer of DeepSeek-V3.2-Exp's sparse attention scores every cached key
+ * position against each query token and keeps the best positions per token:
+ *
+ *   S[t,s] = k_scale[s] * sum_{h<64} w_eff[t,h] * ReLU( q8[t,h,:] . k8[s,:] )
+ *
+ * (page "Index scores": the score formula, with 1/sqrt(64) folded into the
+ * weights and 1/sqrt(128) folded together with each query's fp8 scale; the
+ * fp8_index docstring excerpt: fp8 q @ fp8 k -> fp32 logits, ReLU, times the
+ * folded weights, head sum, times the e8m0 key scale).  Keys and queries reach
+ * fp8 through a scaled Hadamard-128 rotation and a per-128-feature power-of-two
+ * scale (page "Hadamard rotation"; page "Index key cache").  Masked positions
+ * get -inf and each row keeps its top-k positions (Indexer.forward excerpt).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE memory owned by the caller (for example
+ *     PyTorch tensors).  The library never allocates, frees, copies to the host
+ *     or synchronizes; each call only enqueues kernels on `stream` and returns.
+ *   - `lk_rows` structures are HOST memory, read during the call only.
+ *   - Validation happens on the host before any HIP call; a failed validation
+ *     enqueues nothing.  LK_E_HIP reports a failed kernel launch
+ *     (hipGetLastError() after the launch).
+ *   - bf16 data is passed as its uint16 bit pattern; fp8 data is e4m3fn bytes.
+ *   - The library keeps no state, prints nothing and never aborts; calls are
+ *     thread-safe.  Non-finite inputs are outside the contract.
+ *   - Zero-sized work (no rows, no keys) returns LK_OK and enqueues nothing.
+ */
+#ifndef LK_H
+#define LK_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LK_API __attribute__((visibility("default")))
+
+#define LK_ABI_VERSION 1
+#define LK_DIM 128          /* features per index head and per key (page "Index scores") */
+#define LK_HEADS 64         /* index heads (page "Index scores")                       */
+#define LK_TOPK_MAX_T 16384 /* longest score row lk_topk accepts (one row in LDS)      */
+
+typedef enum lk_status {
+    LK_OK = 0,
+    LK_E_NULL = -1,        /* a required pointer is NULL                               */
+    LK_E_SHAPE = -2,       /* negative size, or sizes that do not fit together          */
+    LK_E_UNSUPPORTED = -3, /* valid request outside what this build implements:
+                              heads != 64 in lk_index_score, T > LK_TOPK_MAX_T in
+                              lk_topk, or a pointer not aligned to 16 bytes (4 for
+                              float tensors)                                           */
+    LK_E_HIP = -4          /* the HIP runtime rejected a kernel launch                 */
+} lk_status;
+
+/*
+ * Which (sequence b, query token t, key s) triples are valid.  Valid keys always
+ * form a prefix [0, L) of the score row of (b, t), with
+ *
+ *   L(b,t) = min( T,  seq_len ? clamp(seq_len[b], 0, T) : T,
+ *                 causal ? start_pos + t + 1 : T )          (clamped below at 0)
+ *
+ * Slots L <= s < T of the score row are -inf (Indexer.forward adds the causal
+ * mask; a ragged batch masks each sequence's unused cache slots the same way).
+ */
+typedef struct lk_rows {
+    int32_t B;               /* sequences                                            */
+    int32_t S;               /* query tokens per sequence in this call (decode: 1)   */
+    int64_t T;               /* key slots per score row (= end_pos)                  */
+    int64_t start_pos;       /* absolute position of query token 0 (causal masking)  */
+    const int32_t *seq_len;  /* DEVICE [B] valid cache length per sequence, or NULL  */
+    int32_t causal;          /* nonzero: key s > start_pos + t is masked              */
+} lk_rows;
+
+/*
+ * Key write: rotate_activation + act_quant + cache write of Indexer.forward
+ * (page "Hadamard rotation": kbar = ktilde (1/sqrt 128) H_128 with a bf16 result,
+ * then fp8 quantization in groups of 128 features; page "Index key cache": an
+ * e4m3fn cache [B, T, 128] plus one float32 scale per position).
+ *
+ * For each sequence b < n_seq and row i < n_rows, the 128 bf16 values at
+ *   x + (b * x_seq_stride + i) * 128
+ * are rotated with Sylvester's Hadamard-128 (exact sum, one fp64 multiply by
+ * fl64(128^-0.5), one round-to-nearest-even to bf16), scaled by the smallest
+ * power of two 2^j (j >= -126) with amax <= 448 * 2^j, and encoded as e4m3fn
+ * (nearest-even, sign kept, never NaN).  The 128 bytes go to cache row
+ *   p = (positions ? positions[b] : row_offset) + i
+ * at  cache + (b * cache_seq_stride + p) * 128, and 2^j to
+ * cache_scale[b * cache_seq_stride + p].  Rows with p outside [0, cache_rows)
+ * are skipped (not written).  positions is DEVICE [n_seq] int32 or NULL.
+ * Results are bit-exact for every row whose nonzero magnitudes span at most
+ * 2^38 and whose values are below 2^120 in magnitude.
+ * Requires: cache_rows <= cache_seq_stride; x and cache 16-byte aligned.
+ */
+LK_API lk_status lk_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_rows,
+                                  int64_t x_seq_stride, uint8_t *cache, float *cache_scale,
+                                  int64_t cache_seq_stride, int64_t cache_rows,
+                                  int64_t row_offset, const int32_t *positions,
+                                  hipStream_t stream);
+
+/*
+ * Query side of Indexer.forward: rotate_activation + act_quant of every head
+ * row (same recipe as lk_quantize_keys, one 128-feature group per head) and
+ * the weight fold
+ *   w_eff = fl32( fl32(w * q_scale) * fl32(128^-0.5) )
+ * (page "Index scores": 1/sqrt(128) is folded with each query's fp8 scale; `w`
+ * already carries the 1/sqrt(64) factor).
+ *   q      [n_tokens, heads, 128] bf16 bits     -> q_fp8 [n_tokens, heads, 128]
+ *   w      [n_tokens, heads] float32           -> w_eff [n_tokens, heads] float32
+ *   q_scale (optional, may be NULL) receives the [n_tokens, heads] scales 2^j.
+ * Requires q and q_fp8 16-byte aligned.
+ */
+LK_API lk_status lk_quantize_queries(const uint16_t *q, const float *w, int64_t n_tokens,
+                                     int32_t heads, uint8_t *q_fp8, float *w_eff,
+                                     float *q_scale, hipStream_t stream);
+
+/*
+ * fp8_index + mask (page "Index scores"): for every valid (b, t, s)
+ *   scores[(b*S + t)*T + s] = k_scale[b*cache_seq_stride + s]
+ *        * sum_h w_eff[(b*S + t)*heads + h] * ReLU( q8[(b*S+t), h, :] . k8[b, s, :] )
+ * and -inf (0xFF800000) for masked slots (see lk_rows).
+ *   q_fp8  [B, S, heads, 128] e4m3fn;  w_eff [B, S, heads] float32 (folded)
+ *   k_cache: key s of sequence b at k_cache + (b*cache_seq_stride + s)*128
+ *   k_scale: float32 power-of-two scale of the same key at b*cache_seq_stride + s
+ *   scores [B, S, T] float32.
+ * The fp8 values are converted exactly to f16 and contracted on the MFMA unit
+ * with float32 accumulation; ReLU, the head weighting and sum, the key scale and
+ * the mask are applied in registers; each score is written once.
+ * Requires heads == 64 (else LK_E_UNSUPPORTED), T <= cache_seq_stride,
+ * q_fp8 and k_cache 16-byte aligned, w_eff 16-byte aligned.
+ */
+LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_t heads,
+                                const uint8_t *k_cache, const float *k_scale,
+                                int64_t cache_seq_stride, const lk_rows *rows,
+                                float *scores, hipStream_t stream);
+
+/*
+ * Per-row top-k of Indexer.forward (index_score.topk), with the NKI indexer's
+ * int32 unordered-set result (page "DeepSeek-V3.2 Sparse Indexer Kernel API
+ * Reference", Notes).  For row r = b*S + t with valid length L (see lk_rows):
+ * idx[r*k + j] for j < min(k, L) holds the indices of the min(k, L) largest
+ * scores among scores[r*T + 0 .. r*T + L-1]; ties go to the lower index and
+ * -0 equals +0.  Slots j >= min(k, L) hold -1.  The set is written as: all
+ * indices with a score strictly above the k-th largest, in increasing index
+ * order, then the tied ones, in increasing index order.
+ * Requires k >= 1 and T <= LK_TOPK_MAX_T (else LK_E_UNSUPPORTED).
+ */
+LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, int32_t *idx,
+                         hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+LK_API const char *lk_status_string(lk_status s);
+
+/* LK_ABI_VERSION of the built library. */
+LK_API int32_t lk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LK_H */

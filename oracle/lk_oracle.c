@@ -74,14 +74,22 @@ double lko_e4m3_decode(uint8_t code)
 /* Nearest finite e4m3fn code to v by exhaustive search over the 127 non-negative
  * finite codes (they are ordered by magnitude); on a tie the code whose mantissa
  * LSB is 0 wins; the sign bit copies v's sign.  |v| must not exceed 448. */
+static double e4m3_pos_tab[0x7F];
+static int e4m3_pos_tab_ready = 0;
+
 int lko_e4m3_encode(double v, uint8_t *out)
 {
     double a = fabs(v), best_d = INFINITY;
     int best = -1;
     if (!(a <= 448.0))
         return LKO_E_RANGE;
+    if (!e4m3_pos_tab_ready) {             /* the 127 non-negative finite values, by code */
+        for (int c = 0; c <= 0x7E; c++)
+            e4m3_pos_tab[c] = lko_e4m3_decode((uint8_t)c);
+        e4m3_pos_tab_ready = 1;
+    }
     for (int c = 0; c <= 0x7E; c++) {
-        double d = fabs(lko_e4m3_decode((uint8_t)c) - a);
+        double d = fabs(e4m3_pos_tab[c] - a);
         if (d < best_d || (d == best_d && (c & 1) == 0)) {
             best_d = d;
             best = c;
@@ -163,12 +171,16 @@ static int is_pow2(int d) { return d > 0 && (d & (d - 1)) == 0; }
 /* Rotate one row before any rounding to bf16: p_j = fl64(r_j * C) with
  * r_j = sum_i H[j][i] x_i summed exactly (reading R3).  The fp64 sum is exact when
  * the row's nonzero magnitudes span at most 2^38 (8-bit significands, at most
- * 7 bits of carry, 53-bit accumulator); wider rows return LKO_E_RANGE. */
+ * 7 bits of carry, 53-bit accumulator); wider rows return LKO_E_RANGE.  d <= 512.
+ * Not thread-safe (the matrix table is shared). */
+static double hadamard_tab[512 * 512];
+static int hadamard_d = 0;
+
 int lko_rotate_row(const uint16_t *x_bf16, int d, double *p_out)
 {
     int emin = 100000, emax = -100000;
-    double C;
-    if (!is_pow2(d) || d > 4096)
+    double C, xd[512];
+    if (!is_pow2(d) || d > 512)
         return LKO_E_ARG;
     for (int i = 0; i < d; i++) {
         double v = lko_bf16_decode(x_bf16[i]);
@@ -184,10 +196,18 @@ int lko_rotate_row(const uint16_t *x_bf16, int d, double *p_out)
     if (emax >= emin && emax - emin > 38)
         return LKO_E_RANGE;
     C = lko_rotation_scale(d);
+    for (int i = 0; i < d; i++)
+        xd[i] = lko_bf16_decode(x_bf16[i]);
+    if (hadamard_d != d) {                 /* tabulate H_d once from its definition */
+        for (int j = 0; j < d; j++)
+            for (int i = 0; i < d; i++)
+                hadamard_tab[j * d + i] = (double)lko_hadamard_entry(j, i);
+        hadamard_d = d;
+    }
     for (int j = 0; j < d; j++) {
         double r = 0.0;
         for (int i = 0; i < d; i++)
-            r += (double)lko_hadamard_entry(j, i) * lko_bf16_decode(x_bf16[i]);
+            r += hadamard_tab[j * d + i] * xd[i];
         if (r == 0.0)
             r = 0.0;               /* the exact sum zero is the real zero: +0 (R5) */
         p_out[j] = r * C;
@@ -209,7 +229,7 @@ int lko_scale_exponent(double amax)
  * codes[d] receives the bytes, *scale the float32 scale 2^j. */
 int lko_quantize_row(const uint16_t *x_bf16, int d, uint8_t *codes, float *scale)
 {
-    double p[4096], y[4096], amax = 0.0;
+    double p[512], y[512], amax = 0.0;
     int rc, j;
     rc = lko_rotate_row(x_bf16, d, p);
     if (rc != LKO_OK)

@@ -1,0 +1,9 @@
+"""Lightning-indexer hot path for MI355X (gfx950): key write, fp8 index score with
+mask, and per-row top-k, as hand-written HIP kernels behind a C ABI (include/lk.h).
+
+The Python functions below only marshal torch tensors into that ABI.
+"""
+from ._lib import LkError, LkRows  # noqa: F401
+from .api import lk_index_score, lk_quantize_keys, lk_quantize_queries, lk_topk  # noqa: F401
+
+__all__ = ["lk_quantize_keys", "lk_quantize_queries", "lk_index_score", "lk_topk", "LkError", "LkRows"]

@@ -1,0 +1,139 @@
+"""Python binding of the lightning-indexer C ABI (include/lk.h).
+
+Each function checks dtypes, shapes and devices of its torch tensors, allocates
+outputs the caller did not pass, and forwards pointers, sizes and the current HIP
+stream to the C entry point of the same name.  All computation happens in liblk's
+kernels; there is no CPU path.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import LkRows
+
+DIM = 128
+HEADS = 64
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _byte_view(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def _rows(B: int, S: int, T: int, start_pos: int, seq_len: Optional[torch.Tensor], causal: bool) -> LkRows:
+    ptr = None
+    if seq_len is not None:
+        _need(seq_len.dtype == torch.int32 and seq_len.is_cuda and seq_len.is_contiguous()
+              and seq_len.numel() >= B, "seq_len must be a contiguous int32 CUDA tensor with B entries")
+        ptr = seq_len.data_ptr()
+    return LkRows(B, S, T, start_pos, ptr, 1 if causal else 0)
+
+
+def lk_quantize_keys(x: torch.Tensor, cache: torch.Tensor, cache_scale: torch.Tensor,
+                     row_offset: int = 0, positions: Optional[torch.Tensor] = None) -> None:
+    """Rotate + quantize x [n_seq, n_rows, 128] (bf16) into cache [N, cap, 128] (uint8 or
+    float8_e4m3fn) and cache_scale [N, cap] or [N, cap, 1] (float32), rows starting at
+    `row_offset` or at positions[b] (int32 CUDA [n_seq])."""
+    _need(x.dtype == torch.bfloat16 and x.dim() == 3 and x.shape[2] == DIM, "x must be bf16 [n_seq, n_rows, 128]")
+    _need(x.stride(2) == 1 and x.stride(1) == DIM and x.stride(0) % DIM == 0, "x rows must be contiguous")
+    cache = _byte_view(cache)
+    _need(cache.dtype == torch.uint8 and cache.dim() == 3 and cache.shape[2] == DIM
+          and cache.stride(2) == 1 and cache.stride(1) == DIM and cache.stride(0) % DIM == 0,
+          "cache must be uint8/e4m3fn [N, cap, 128] with contiguous rows")
+    cs = cache_scale.squeeze(-1) if cache_scale.dim() == 3 else cache_scale
+    seq_stride = cache.stride(0) // DIM
+    _need(cs.dtype == torch.float32 and cs.dim() == 2 and cs.shape[:2] == cache.shape[:2]
+          and cs.stride(1) == 1 and (cs.shape[0] == 1 or cs.stride(0) == seq_stride),
+          "cache_scale must be float32 [N, cap] sharing the cache's sequence stride")
+    _need(x.shape[0] <= cache.shape[0], "more sequences than cache slots")
+    _need(x.is_cuda and cache.device == x.device and cs.device == x.device, "tensors must be on one CUDA device")
+    pos_ptr = None
+    if positions is not None:
+        _need(positions.dtype == torch.int32 and positions.is_cuda and positions.is_contiguous()
+              and positions.numel() >= x.shape[0], "positions must be int32 CUDA [n_seq]")
+        pos_ptr = positions.data_ptr()
+    st = _lib.load().lk_quantize_keys(x.data_ptr(), x.shape[0], x.shape[1], x.stride(0) // DIM,
+                                      cache.data_ptr(), cs.data_ptr(), seq_stride, cache.shape[1],
+                                      row_offset, pos_ptr, _stream(x))
+    _lib.check("lk_quantize_keys", st)
+
+
+def lk_quantize_queries(q: torch.Tensor, w: torch.Tensor, q_fp8: Optional[torch.Tensor] = None,
+                        w_eff: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None):
+    """q [..., H, 128] bf16 and w [..., H] float32 -> (q_fp8 uint8 [..., H, 128], w_eff float32 [..., H]).
+    If `q_scale` (float32 [..., H]) is given it receives the per-head scales."""
+    _need(q.dtype == torch.bfloat16 and q.shape[-1] == DIM and q.is_contiguous(), "q must be contiguous bf16 [..., H, 128]")
+    _need(w.dtype == torch.float32 and w.shape == q.shape[:-1] and w.is_contiguous(), "w must be contiguous float32 [..., H]")
+    H = q.shape[-2]
+    n_tok = q.numel() // (H * DIM) if H > 0 else 0
+    if q_fp8 is None:
+        q_fp8 = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    if w_eff is None:
+        w_eff = torch.empty(w.shape, dtype=torch.float32, device=q.device)
+    q8 = _byte_view(q_fp8)
+    _need(q8.shape == q.shape and q8.is_contiguous() and w_eff.shape == w.shape and w_eff.is_contiguous(),
+          "output shapes must match the inputs")
+    qs_ptr = None
+    if q_scale is not None:
+        _need(q_scale.dtype == torch.float32 and q_scale.shape == w.shape and q_scale.is_contiguous(), "bad q_scale")
+        qs_ptr = q_scale.data_ptr()
+    st = _lib.load().lk_quantize_queries(q.data_ptr(), w.data_ptr(), n_tok, H, q8.data_ptr(),
+                                         w_eff.data_ptr(), qs_ptr, _stream(q))
+    _lib.check("lk_quantize_queries", st)
+    return q_fp8, w_eff
+
+
+def lk_index_score(q_fp8: torch.Tensor, w_eff: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor,
+                   T: int, start_pos: int = 0, seq_len: Optional[torch.Tensor] = None, causal: bool = False,
+                   scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Masked fp8 index scores [B, S, T] (float32) of q_fp8 [B, S, 64, 128] against keys
+    [0, T) of k_cache [>=B, cap, 128] with scales k_scale [>=B, cap] (or [.., cap, 1])."""
+    q8 = _byte_view(q_fp8)
+    kc = _byte_view(k_cache)
+    _need(q8.dtype == torch.uint8 and q8.dim() == 4 and q8.shape[3] == DIM and q8.is_contiguous(),
+          "q_fp8 must be contiguous [B, S, H, 128]")
+    B, S, H = q8.shape[:3]
+    _need(w_eff.dtype == torch.float32 and tuple(w_eff.shape) == (B, S, H) and w_eff.is_contiguous(), "bad w_eff")
+    _need(kc.dtype == torch.uint8 and kc.dim() == 3 and kc.shape[2] == DIM and kc.stride(2) == 1
+          and kc.stride(1) == DIM and kc.stride(0) % DIM == 0 and kc.shape[0] >= B, "bad k_cache")
+    ks = k_scale.squeeze(-1) if k_scale.dim() == 3 else k_scale
+    seq_stride = kc.stride(0) // DIM
+    _need(ks.dtype == torch.float32 and ks.dim() == 2 and ks.shape[:2] == kc.shape[:2] and ks.stride(1) == 1
+          and (ks.shape[0] == 1 or ks.stride(0) == seq_stride), "k_scale must share k_cache's sequence stride")
+    _need(0 <= T <= kc.shape[1], "T exceeds the cache capacity")
+    if scores is None:
+        scores = torch.empty((B, S, T), dtype=torch.float32, device=q8.device)
+    _need(scores.dtype == torch.float32 and tuple(scores.shape) == (B, S, T) and scores.is_contiguous(), "bad scores")
+    rows = _rows(B, S, T, start_pos, seq_len, causal)
+    st = _lib.load().lk_index_score(q8.data_ptr(), w_eff.data_ptr(), H, kc.data_ptr(), ks.data_ptr(),
+                                    seq_stride, ctypes.byref(rows), scores.data_ptr(), _stream(q8))
+    _lib.check("lk_index_score", st)
+    return scores
+
+
+def lk_topk(scores: torch.Tensor, k: int, start_pos: int = 0, seq_len: Optional[torch.Tensor] = None,
+            causal: bool = False, idx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Indices [B, S, k] (int32) of the min(k, L) largest scores of each row's valid
+    prefix [0, L); unused slots are -1."""
+    _need(scores.dtype == torch.float32 and scores.dim() == 3 and scores.is_contiguous(),
+          "scores must be contiguous float32 [B, S, T]")
+    B, S, T = scores.shape
+    if idx is None:
+        idx = torch.empty((B, S, k), dtype=torch.int32, device=scores.device)
+    _need(idx.dtype == torch.int32 and tuple(idx.shape) == (B, S, k) and idx.is_contiguous(), "bad idx")
+    rows = _rows(B, S, T, start_pos, seq_len, causal)
+    st = _lib.load().lk_topk(scores.data_ptr(), ctypes.byref(rows), k, idx.data_ptr(), _stream(scores))
+    _lib.check("lk_topk", st)
+    return idx

@@ -1,0 +1,122 @@
+// lk_api.hip -- host side of the C ABI declared in include/lk.h: argument validation
+// (before any HIP call) and kernel dispatch on the caller's stream.
+#include <stdint.h>
+
+#include "lk_device.h"
+
+namespace lk {
+hipError_t launch_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride,
+                                uint8_t *cache, float *cache_scale, int64_t cache_seq_stride,
+                                int64_t cache_rows, int64_t row_offset, const int32_t *positions,
+                                hipStream_t stream);
+hipError_t launch_quantize_queries(const uint16_t *q, const float *w, int64_t n_rows, uint8_t *q_fp8,
+                                   float *w_eff, float *q_scale, hipStream_t stream);
+hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
+                              const float *k_scale, int64_t cache_seq_stride, const RowsDev &rows,
+                              float *scores, hipStream_t stream);
+hipError_t launch_topk(const float *scores, const RowsDev &rows, int32_t k, int32_t *idx, hipStream_t stream);
+}  // namespace lk
+
+namespace {
+
+constexpr int64_t kMaxGridX = 0x7FFFFFFFLL;
+constexpr int64_t kMaxGridYZ = 65535;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+lk_status from_hip(hipError_t e) { return e == hipSuccess ? LK_OK : LK_E_HIP; }
+
+lk_status check_rows(const lk_rows *rows) {
+    if (!rows) return LK_E_NULL;
+    if (rows->B < 0 || rows->S < 0 || rows->T < 0) return LK_E_SHAPE;
+    return LK_OK;
+}
+
+lk::RowsDev to_dev(const lk_rows &r) {
+    lk::RowsDev d;
+    d.B = r.B;
+    d.S = r.S;
+    d.T = r.T;
+    d.start_pos = r.start_pos;
+    d.seq_len = r.seq_len;
+    d.causal = r.causal;
+    return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+LK_API lk_status lk_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride,
+                                  uint8_t *cache, float *cache_scale, int64_t cache_seq_stride,
+                                  int64_t cache_rows, int64_t row_offset, const int32_t *positions,
+                                  hipStream_t stream) {
+    if (n_seq < 0 || n_rows < 0 || x_seq_stride < 0 || cache_seq_stride < 0 || cache_rows < 0)
+        return LK_E_SHAPE;
+    if (cache_rows > cache_seq_stride) return LK_E_SHAPE;
+    if (n_seq == 0 || n_rows == 0) return LK_OK;
+    if (!x || !cache || !cache_scale) return LK_E_NULL;
+    if (!aligned(x, 16) || !aligned(cache, 16) || !aligned(cache_scale, 4) || !aligned(positions, 4))
+        return LK_E_UNSUPPORTED;
+    if (n_rows > INT64_MAX / n_seq || (n_seq * n_rows + 31) / 32 > kMaxGridX) return LK_E_UNSUPPORTED;
+    return from_hip(lk::launch_quantize_keys(x, n_seq, n_rows, x_seq_stride, cache, cache_scale,
+                                             cache_seq_stride, cache_rows, row_offset, positions, stream));
+}
+
+LK_API lk_status lk_quantize_queries(const uint16_t *q, const float *w, int64_t n_tokens, int32_t heads,
+                                     uint8_t *q_fp8, float *w_eff, float *q_scale, hipStream_t stream) {
+    if (n_tokens < 0 || heads < 1) return LK_E_SHAPE;
+    if (n_tokens == 0) return LK_OK;
+    if (!q || !w || !q_fp8 || !w_eff) return LK_E_NULL;
+    if (!aligned(q, 16) || !aligned(q_fp8, 16) || !aligned(w, 4) || !aligned(w_eff, 4) || !aligned(q_scale, 4))
+        return LK_E_UNSUPPORTED;
+    if (n_tokens > INT64_MAX / heads) return LK_E_UNSUPPORTED;
+    const int64_t n_rows = n_tokens * heads;
+    if ((n_rows + 31) / 32 > kMaxGridX) return LK_E_UNSUPPORTED;
+    return from_hip(lk::launch_quantize_queries(q, w, n_rows, q_fp8, w_eff, q_scale, stream));
+}
+
+LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_t heads,
+                                const uint8_t *k_cache, const float *k_scale, int64_t cache_seq_stride,
+                                const lk_rows *rows, float *scores, hipStream_t stream) {
+    lk_status st = check_rows(rows);
+    if (st != LK_OK) return st;
+    if (cache_seq_stride < 0 || rows->T > cache_seq_stride) return LK_E_SHAPE;
+    if (heads != LK_HEADS) return LK_E_UNSUPPORTED;
+    if (rows->B == 0 || rows->S == 0 || rows->T == 0) return LK_OK;
+    if (!q_fp8 || !w_eff || !k_cache || !k_scale || !scores) return LK_E_NULL;
+    if (!aligned(q_fp8, 16) || !aligned(w_eff, 16) || !aligned(k_cache, 16) || !aligned(k_scale, 4) ||
+        !aligned(scores, 4) || !aligned(rows->seq_len, 4))
+        return LK_E_UNSUPPORTED;
+    if (rows->B > kMaxGridYZ || (rows->S + 7) / 8 > kMaxGridYZ) return LK_E_UNSUPPORTED;
+    if (rows->T > kMaxGridX) return LK_E_UNSUPPORTED;
+    return from_hip(lk::launch_index_score(q_fp8, w_eff, k_cache, k_scale, cache_seq_stride, to_dev(*rows),
+                                           scores, stream));
+}
+
+LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, int32_t *idx, hipStream_t stream) {
+    lk_status st = check_rows(rows);
+    if (st != LK_OK) return st;
+    if (k < 1) return LK_E_SHAPE;
+    if (rows->T > LK_TOPK_MAX_T) return LK_E_UNSUPPORTED;
+    if (rows->B == 0 || rows->S == 0) return LK_OK;
+    if (!scores || !idx) return LK_E_NULL;
+    if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(rows->seq_len, 4)) return LK_E_UNSUPPORTED;
+    if ((int64_t)rows->B * rows->S > kMaxGridX) return LK_E_UNSUPPORTED;
+    return from_hip(lk::launch_topk(scores, to_dev(*rows), k, idx, stream));
+}
+
+LK_API const char *lk_status_string(lk_status s) {
+    switch (s) {
+    case LK_OK: return "LK_OK";
+    case LK_E_NULL: return "LK_E_NULL: a required pointer is NULL";
+    case LK_E_SHAPE: return "LK_E_SHAPE: sizes are negative or do not fit together";
+    case LK_E_UNSUPPORTED: return "LK_E_UNSUPPORTED: outside what this build implements (heads, row length, alignment or grid limits)";
+    case LK_E_HIP: return "LK_E_HIP: the HIP runtime rejected a kernel launch";
+    }
+    return "unknown lk_status";
+}
+
+LK_API int32_t lk_abi_version(void) { return LK_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// lk_device.h -- device-side helpers shared by the gfx950 kernels of liblk.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lk.h"
+
+namespace lk {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// Row-validity parameters passed by value to kernels (mirror of lk_rows).
+struct RowsDev {
+    int32_t B, S;
+    int64_t T, start_pos;
+    const int32_t *seq_len;
+    int32_t causal;
+};
+
+// Valid prefix length of score row (b, t): min(T, seq_len[b], start_pos + t + 1).
+__device__ __forceinline__ int64_t row_len(const RowsDev &r, int b, int64_t t) {
+    int64_t L = r.T;
+    if (r.seq_len) {
+        int64_t s = r.seq_len[b];
+        if (s < L) L = s;
+    }
+    if (r.causal) {
+        int64_t c = r.start_pos + t + 1;
+        if (c < L) L = c;
+    }
+    return L < 0 ? 0 : L;
+}
+
+// Four e4m3fn bytes -> four f16 (exact: every e4m3fn value is an f16 normal or zero).
+__device__ __forceinline__ void fp8x4_to_f16(uint32_t v, _Float16 *o) {
+    half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+    half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
+    o[0] = lo[0];
+    o[1] = lo[1];
+    o[2] = hi[0];
+    o[3] = hi[1];
+}
+
+// Eight e4m3fn bytes (two dwords) -> one f16x8 MFMA operand.
+__device__ __forceinline__ half8 fp8x8_to_half8(uint32_t a, uint32_t b) {
+    half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false);
+    half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true);
+    half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
+    half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true);
+    half8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    return r;
+}
+
+// Sum across the two 32-lane halves of a wave for two values at once:
+// returns, in lanes 0-31, x[l] + x[l+32], and in lanes 32-63, y[l-32] + y[l].
+__device__ __forceinline__ float halves_sum_pair(float x, float y) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace lk

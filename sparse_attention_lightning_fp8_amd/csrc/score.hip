@@ -1,0 +1,258 @@
+// score.hip -- fp8 index score + mask for the lightning indexer (gfx950).
+//
+// Page "Index scores": S[t,s] = sum_h w[t,h] ReLU(Qbar[h,t] . kbar[s]) / (sqrt 64 sqrt 128);
+// the fp8_index docstring computes it as fp8 q @ fp8 k -> fp32 logits, ReLU, times the
+// folded weights, head sum, times the e8m0 key scale.  Indexer.forward then adds the
+// mask (-inf outside each row's valid prefix).
+//
+// The contraction Q[64 x 128] x K^T[128 x keys] runs on v_mfma_f32_32x32x16_f16 with
+// the e4m3fn bytes converted exactly to f16 in registers (v_cvt_scalef32_pk_f16_fp8,
+// scale 1): the fp8 MFMA of gfx950 sums each group of products at reduced width and
+// misses the 1e-5 relative accuracy this path is held to, while every e4m3fn value
+// is an f16 normal and every f16 product is exact in the float32 accumulator.
+//
+// Operand layout (one wave, 32x32x16 f16): lane l supplies row (l % 32) of A (a head)
+// and column (l % 32) of B (a key); lanes 0-31 carry bytes [0, 64) of the 128-byte row
+// and lanes 32-63 bytes [64, 128), 8 bytes per K-step, so K-step kk pairs features
+// 8kk..8kk+7 and 64+8kk..64+8kk+7 of both operands.  The accumulator of M-tile m
+// (heads 32m..32m+31) holds, in lane l, key (l % 32) and heads
+// 32m + 8(i/4) + 4(l/32) + (i%4) for i < 16, so a lane sums 32 heads in registers and
+// one cross-half swap (v_permlane32_swap) completes the 64-head sum.
+#include "lk_device.h"
+
+namespace lk {
+namespace {
+
+// Per-lane A operand (64 heads x 128 features of one query token) as f16, and the
+// matching folded weights: A[m][kk] is the K-step kk operand of M-tile m.
+struct QueryFrag {
+    half8 a[2][8];
+    float w[2][16];
+};
+
+__device__ __forceinline__ void load_query(const uint8_t *__restrict__ q_row /*64 x 128*/,
+                                           const float *__restrict__ w_row /*64*/, int lane,
+                                           QueryFrag &f) {
+    const int r = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(q_row + (32 * m + r) * LK_DIM + 64 * hh);
+        uint4 v[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) v[c] = src[c];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            f.a[m][2 * c] = fp8x8_to_half8(v[c].x, v[c].y);
+            f.a[m][2 * c + 1] = fp8x8_to_half8(v[c].z, v[c].w);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const float4 wv = *reinterpret_cast<const float4 *>(w_row + 32 * m + 8 * g + 4 * hh);
+            f.w[m][4 * g + 0] = wv.x;
+            f.w[m][4 * g + 1] = wv.y;
+            f.w[m][4 * g + 2] = wv.z;
+            f.w[m][4 * g + 3] = wv.w;
+        }
+    }
+}
+
+// Head-weighted ReLU sum of the two M-tile accumulators (this lane's 32 heads).
+__device__ __forceinline__ float relu_weighted_sum(const float16v acc[2], const QueryFrag &f) {
+    float s = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) s += __builtin_fmaxf(acc[m][i], 0.0f) * f.w[m][i];
+    return s;
+}
+
+// ------------------------------------------------------------------ decode (S == 1)
+// One wave scores 128 consecutive keys (4 tiles of 32) of one query row; a block of
+// 4 waves covers 512 keys.  Each lane loads its 4 x 64 bytes of K straight into the
+// B-operand registers (keys are read exactly once, so LDS brings no reuse here).
+constexpr int kDecWaves = 4;
+constexpr int kDecTiles = 4;                       // 32-key tiles per wave
+constexpr int kDecKeysPerWave = 32 * kDecTiles;    // 128
+constexpr int kDecKeysPerBlock = kDecKeysPerWave * kDecWaves;
+
+__global__ void __launch_bounds__(256)
+score_decode_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict__ w_eff,
+                    const uint8_t *__restrict__ k_cache, const float *__restrict__ k_scale,
+                    int64_t cache_seq_stride, RowsDev rows, float *__restrict__ scores) {
+    const int lane = __lane_id();
+    const int wave = threadIdx.x >> 6;
+    const int qrow = blockIdx.y;                       // b * S + t
+    const int b = qrow / rows.S;
+    const int t = qrow - b * rows.S;
+    const int64_t T = rows.T;
+    const int64_t L = row_len(rows, b, t);
+    const int64_t key0 = (int64_t)blockIdx.x * kDecKeysPerBlock + (int64_t)wave * kDecKeysPerWave;
+    if (key0 >= T) return;
+    float *out = scores + (int64_t)qrow * T;
+    if (key0 >= L) {                                   // fully masked: -inf only
+#pragma unroll
+        for (int p = 0; p < kDecTiles / 2; p++) {
+            const int64_t s = key0 + 64 * p + lane;
+            if (s < T) out[s] = -__builtin_inff();
+        }
+        return;
+    }
+    const int r = lane & 31, hh = lane >> 5;
+    const uint8_t *kbase = k_cache + (int64_t)b * cache_seq_stride * LK_DIM;
+    // Issue the K loads first (the long-latency HBM stream), then Q and w.
+    uint4 kv[kDecTiles][4];
+#pragma unroll
+    for (int j = 0; j < kDecTiles; j++) {
+        const int64_t s = key0 + 32 * j + r;
+        if (s < L) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(kbase + s * LK_DIM + 64 * hh);
+#pragma unroll
+            for (int c = 0; c < 4; c++) kv[j][c] = src[c];
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; c++) kv[j][c] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    float ks[kDecTiles / 2];
+#pragma unroll
+    for (int p = 0; p < kDecTiles / 2; p++) {
+        const int64_t s = key0 + 64 * p + lane;
+        ks[p] = s < L ? k_scale[(int64_t)b * cache_seq_stride + s] : 0.0f;
+    }
+    QueryFrag f;
+    load_query(q_fp8 + (int64_t)qrow * LK_HEADS * LK_DIM, w_eff + (int64_t)qrow * LK_HEADS, lane, f);
+
+    float part[kDecTiles];
+#pragma unroll
+    for (int j = 0; j < kDecTiles; j++) {
+        float16v acc[2] = {};
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const half8 b0 = fp8x8_to_half8(kv[j][c].x, kv[j][c].y);
+            const half8 b1 = fp8x8_to_half8(kv[j][c].z, kv[j][c].w);
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][2 * c], b0, acc[m], 0, 0, 0);
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][2 * c + 1], b1, acc[m], 0, 0, 0);
+            }
+        }
+        part[j] = relu_weighted_sum(acc, f);
+    }
+#pragma unroll
+    for (int p = 0; p < kDecTiles / 2; p++) {
+        // lanes 0-31: tile 2p, key l; lanes 32-63: tile 2p+1, key l-32  ->  key key0 + 64p + l
+        const float sum = halves_sum_pair(part[2 * p], part[2 * p + 1]);
+        const int64_t s = key0 + 64 * p + lane;
+        if (s < T) out[s] = s < L ? sum * ks[p] : -__builtin_inff();
+    }
+}
+
+// ------------------------------------------------------------------ prefill (S > 1)
+// A block of 8 waves owns 8 consecutive query tokens of one sequence (one per wave)
+// and a chunk of 256 keys.  The chunk is read from HBM once per block, converted to
+// f16 once, and kept in LDS; every wave then streams it through the MFMA against
+// its own query held in registers.
+constexpr int kPreWaves = 8;
+constexpr int kPreChunk = 256;                      // keys per block
+constexpr int kPreRowBytes = 2 * LK_DIM + 16;       // f16 row + 16 B pad against bank conflicts
+
+__global__ void __launch_bounds__(512)
+score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict__ w_eff,
+                     const uint8_t *__restrict__ k_cache, const float *__restrict__ k_scale,
+                     int64_t cache_seq_stride, RowsDev rows, float *__restrict__ scores) {
+    __shared__ __attribute__((aligned(16))) uint8_t sk[kPreChunk * kPreRowBytes];
+    __shared__ float sks[kPreChunk];
+    const int lane = __lane_id();
+    const int wave = threadIdx.x >> 6;
+    const int b = blockIdx.z;
+    const int t0 = blockIdx.y * kPreWaves;
+    const int64_t T = rows.T;
+    const int64_t kc0 = (int64_t)blockIdx.x * kPreChunk;
+    const int t = t0 + wave;
+    const bool has_row = t < rows.S;
+    const int64_t L = has_row ? row_len(rows, b, t) : 0;
+    // The block needs keys below the largest valid length of its rows.
+    const int t_last = (t0 + kPreWaves - 1 < rows.S ? t0 + kPreWaves - 1 : rows.S - 1);
+    const int64_t Lmax = row_len(rows, b, t_last);     // row_len is non-decreasing in t
+    float *out = scores + ((int64_t)b * rows.S + t) * T;
+    if (kc0 >= Lmax) {                                  // whole block masked
+        if (has_row)
+            for (int64_t s = kc0 + lane; s < kc0 + kPreChunk && s < T; s += 64) out[s] = -__builtin_inff();
+        return;
+    }
+    // Stage the chunk: thread i converts half of key (i / 2) to f16.
+    {
+        const int kr = threadIdx.x >> 1, half = threadIdx.x & 1;
+        const int64_t s = kc0 + kr;
+        uint4 v[4];
+        if (s < Lmax) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                k_cache + ((int64_t)b * cache_seq_stride + s) * LK_DIM + 64 * half);
+#pragma unroll
+            for (int c = 0; c < 4; c++) v[c] = src[c];
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; c++) v[c] = make_uint4(0, 0, 0, 0);
+        }
+        half8 *dst = reinterpret_cast<half8 *>(sk + kr * kPreRowBytes + 128 * half);
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            dst[2 * c] = fp8x8_to_half8(v[c].x, v[c].y);
+            dst[2 * c + 1] = fp8x8_to_half8(v[c].z, v[c].w);
+        }
+        if (threadIdx.x < kPreChunk)
+            sks[threadIdx.x] = (kc0 + threadIdx.x < Lmax)
+                                   ? k_scale[(int64_t)b * cache_seq_stride + kc0 + threadIdx.x] : 0.0f;
+    }
+    QueryFrag f;
+    if (has_row) {
+        const int64_t qrow = (int64_t)b * rows.S + t;
+        load_query(q_fp8 + qrow * LK_HEADS * LK_DIM, w_eff + qrow * LK_HEADS, lane, f);
+    }
+    __syncthreads();
+    if (!has_row) return;
+    const int r = lane & 31, hh = lane >> 5;
+    for (int j = 0; j < kPreChunk / 32; j += 2) {
+        if (kc0 + 32 * j >= L) {                        // rest of the row is masked
+            for (int64_t s = kc0 + 32 * j + lane; s < kc0 + kPreChunk && s < T; s += 64) out[s] = -__builtin_inff();
+            break;
+        }
+        float part[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++) {
+            const uint8_t *row = sk + (32 * (j + jj) + r) * kPreRowBytes + 128 * hh;
+            float16v acc[2] = {};
+#pragma unroll
+            for (int kk = 0; kk < 8; kk++) {
+                const half8 bk = *reinterpret_cast<const half8 *>(row + 16 * kk);
+#pragma unroll
+                for (int m = 0; m < 2; m++)
+                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][kk], bk, acc[m], 0, 0, 0);
+            }
+            part[jj] = relu_weighted_sum(acc, f);
+        }
+        const float sum = halves_sum_pair(part[0], part[1]);
+        const int64_t s = kc0 + 32 * j + lane;
+        if (s < T) out[s] = s < L ? sum * sks[32 * j + lane] : -__builtin_inff();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
+                              const float *k_scale, int64_t cache_seq_stride, const RowsDev &rows,
+                              float *scores, hipStream_t stream) {
+    if (rows.S == 1) {
+        dim3 grid((unsigned)((rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock), (unsigned)rows.B);
+        hipLaunchKernelGGL(score_decode_kernel, grid, dim3(64 * kDecWaves), 0, stream, q_fp8, w_eff, k_cache,
+                           k_scale, cache_seq_stride, rows, scores);
+    } else {
+        dim3 grid((unsigned)((rows.T + kPreChunk - 1) / kPreChunk), (unsigned)((rows.S + kPreWaves - 1) / kPreWaves),
+                  (unsigned)rows.B);
+        hipLaunchKernelGGL(score_prefill_kernel, grid, dim3(64 * kPreWaves), 0, stream, q_fp8, w_eff, k_cache,
+                           k_scale, cache_seq_stride, rows, scores);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lk

@@ -1,0 +1,150 @@
+"""Shared parity machinery: the oracle side (CPU, from oracle/ only) and the GPU side
+(through the C ABI only), on the same seeded inputs from the workload generator.
+No value flows from the GPU side into the oracle side."""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from oracle import oracle as O
+from sparse_attention_lightning_fp8_amd import workloads as W
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def tol(ref_finite_max: float) -> float:
+    """Score tolerance: 1e-5 * max|S_ref| + 1e-6 over the compared finite outputs."""
+    return 1e-5 * ref_finite_max + 1e-6
+
+
+# ------------------------------------------------------------------ oracle side
+@dataclass
+class OracleRow:
+    b: int
+    t: int
+    L: int
+    scores: np.ndarray    # float64 [T]
+    topk: np.ndarray      # int32 [k]
+
+
+class OracleCase:
+    """Oracle results for selected query rows of a workload."""
+
+    def __init__(self, inp: W.Inputs):
+        self.inp = inp
+        self.wl = inp.wl
+        self._kq: Dict[int, tuple] = {}
+
+    def keys(self, b: int, n: int):
+        """Oracle quantization of cache rows [0, n) of sequence b."""
+        got = self._kq.get(b)
+        if got is None or got[0].shape[0] < n:
+            bits = W.bf16_bits(self.inp.k[b, :n])
+            codes, scales = O.quantize_rows(bits)
+            self._kq[b] = (codes, scales)
+        codes, scales = self._kq[b]
+        return codes[:n], scales[:n]
+
+    def query(self, b: int, t: int):
+        bits = W.bf16_bits(self.inp.q[b, t])
+        q8, qs = O.quantize_rows(bits)
+        w_eff = O.fold_weights(self.inp.w[b, t].numpy(), qs)
+        return q8, qs, w_eff
+
+    def row_len(self, b: int, t: int) -> int:
+        wl = self.wl
+        sl = max(int(self.inp.lens[b]), 0) if self.inp.lens is not None else -1
+        return O.valid_len(wl.T, sl, wl.causal, wl.start_pos, t)
+
+    def row(self, b: int, t: int) -> OracleRow:
+        wl = self.wl
+        L = self.row_len(b, t)
+        q8, qs, w_eff = self.query(b, t)
+        k8, ks = self.keys(b, max(L, 1))
+        k8_full = np.zeros((wl.T, 128), np.uint8)
+        ks_full = np.ones(wl.T, np.float32)
+        k8_full[:L] = k8[:L]
+        ks_full[:L] = ks[:L]
+        s = O.score_row(q8, w_eff, k8_full, ks_full, wl.T, L)
+        return OracleRow(b, t, L, s, O.topk(s, L, wl.k))
+
+
+# ------------------------------------------------------------------ GPU side
+@dataclass
+class GpuResult:
+    cache: torch.Tensor
+    cache_scale: torch.Tensor
+    q_fp8: torch.Tensor
+    w_eff: torch.Tensor
+    q_scale: torch.Tensor
+    scores: torch.Tensor
+    idx: torch.Tensor
+
+
+def gpu_pipeline(inp: W.Inputs, device="cuda:0", new_rows_only: bool = False) -> GpuResult:
+    """The hot path through the C ABI: cache prefix written first, then one step:
+    key write of the step's rows, query quantize + fold, index score, top-k."""
+    from sparse_attention_lightning_fp8_amd import api
+    wl = inp.wl
+    k = inp.k.to(device)
+    cache = torch.zeros((wl.B, wl.cap, 128), dtype=torch.uint8, device=device)
+    cache_scale = torch.zeros((wl.B, wl.cap), dtype=torch.float32, device=device)
+    positions = inp.positions.to(device)
+    # prefix: every cache row, then the step's own rows again through `positions`
+    api.lk_quantize_keys(k, cache, cache_scale, row_offset=0)
+    rows_step = k.new_empty((wl.B, wl.S, 128))
+    for b in range(wl.B):
+        p0 = int(inp.positions[b])
+        rows_step[b] = k[b, p0:p0 + wl.S]
+    api.lk_quantize_keys(rows_step, cache, cache_scale, positions=positions)
+    q = inp.q.to(device)
+    w = inp.w.to(device)
+    q_scale = torch.empty_like(w)
+    q_fp8, w_eff = api.lk_quantize_queries(q, w, q_scale=q_scale)
+    seq_len = inp.lens.to(device) if inp.lens is not None else None
+    scores = api.lk_index_score(q_fp8, w_eff, cache, cache_scale, wl.T, start_pos=wl.start_pos,
+                                seq_len=seq_len, causal=wl.causal)
+    idx = api.lk_topk(scores, wl.k, start_pos=wl.start_pos, seq_len=seq_len, causal=wl.causal)
+    torch.cuda.synchronize()
+    return GpuResult(cache, cache_scale, q_fp8, w_eff, q_scale, scores, idx)
+
+
+# ------------------------------------------------------------------ comparisons
+def compare_scores(gpu_rows: List[np.ndarray], ref_rows: List[OracleRow]) -> float:
+    """Assert the -inf pattern is exact and finite entries agree within tolerance.
+    Returns max|err| / max|ref| for reporting."""
+    fin_max = max(float(np.max(np.abs(r.scores[np.isfinite(r.scores)]), initial=0.0)) for r in ref_rows)
+    tau = tol(fin_max)
+    worst = 0.0
+    for g, r in zip(gpu_rows, ref_rows):
+        ref_inf = np.isneginf(r.scores)
+        assert np.array_equal(np.isneginf(g), ref_inf), f"-inf pattern differs in row (b={r.b}, t={r.t})"
+        assert np.all(np.isfinite(g[~ref_inf])), f"non-finite score in row (b={r.b}, t={r.t})"
+        err = np.max(np.abs(g[~ref_inf].astype(np.float64) - r.scores[~ref_inf]), initial=0.0)
+        assert err <= tau, f"row (b={r.b}, t={r.t}): max err {err:.3e} > tol {tau:.3e}"
+        worst = max(worst, err)
+    return worst / fin_max if fin_max > 0 else 0.0
+
+
+def compare_topk(gpu_idx: np.ndarray, r: OracleRow, k: int, tau: float) -> None:
+    """Top-k acceptance against the oracle's fp64 scores: same size, no duplicates, all
+    indices valid, and any disagreement only between keys within tau of the boundary."""
+    kr = min(k, r.L)
+    g = gpu_idx[:kr]
+    assert np.all(gpu_idx[kr:] == -1), "padding must be -1"
+    assert len(set(g.tolist())) == kr, "duplicate indices"
+    assert np.all((g >= 0) & (g < r.L)), "index outside the valid prefix"
+    o = r.topk[:kr]
+    if kr == 0:
+        return
+    vk = np.sort(r.scores[o])[0]          # k-th largest oracle score
+    diff = set(g.tolist()) ^ set(o.tolist())
+    for i in diff:
+        assert abs(r.scores[i] - vk) <= tau, f"row (b={r.b}, t={r.t}): index {i} off the boundary by {r.scores[i] - vk:.3e}"

@@ -1,0 +1,112 @@
+"""The C ABI on the host: the library loads, exports every symbol include/lk.h declares,
+and every validation error returns before any HIP call (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_lightning_fp8_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lk.h")
+
+OK, E_NULL, E_SHAPE, E_UNSUP = 0, -1, -2, -3
+A = 0x10000  # a 16-byte aligned fake device address: never dereferenced by these calls
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LK_API\s+[\w\s\*]+?\b(lk_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    assert syms == sorted(["lk_quantize_keys", "lk_quantize_queries", "lk_index_score", "lk_topk",
+                           "lk_status_string", "lk_abi_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+    assert set(declared_symbols()) == set(_lib.SIGNATURES)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.lk_abi_version() == 1
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.lk_status_string(code).decode().startswith(name)
+    assert lib.lk_status_string(7).decode() == "unknown lk_status"
+
+
+def rows(B=1, S=1, T=16, start=0, seq_len=None, causal=0):
+    return ctypes.byref(_lib.LkRows(B, S, T, start, seq_len, causal))
+
+
+def test_quantize_keys_validation(lib):
+    f = lib.lk_quantize_keys
+    assert f(A, -1, 1, 1, A, A, 16, 16, 0, None, None) == E_SHAPE
+    assert f(A, 1, 1, 1, A, A, 16, 17, 0, None, None) == E_SHAPE         # cache_rows > stride
+    assert f(None, 1, 1, 1, A, A, 16, 16, 0, None, None) == E_NULL
+    assert f(A, 1, 1, 1, None, A, 16, 16, 0, None, None) == E_NULL
+    assert f(A, 1, 1, 1, A, None, 16, 16, 0, None, None) == E_NULL
+    assert f(A + 8, 1, 1, 1, A, A, 16, 16, 0, None, None) == E_UNSUP     # misaligned bf16 rows
+    assert f(A, 1, 1, 1, A + 4, A, 16, 16, 0, None, None) == E_UNSUP
+    assert f(A, 1, 1, 1, A, A, 16, 16, 0, A + 2, None) == E_UNSUP        # misaligned positions
+    assert f(None, 0, 5, 0, None, None, 0, 0, 0, None, None) == OK        # empty: nothing to do
+
+
+def test_quantize_queries_validation(lib):
+    f = lib.lk_quantize_queries
+    assert f(A, A, -1, 64, A, A, None, None) == E_SHAPE
+    assert f(A, A, 1, 0, A, A, None, None) == E_SHAPE
+    assert f(None, A, 1, 64, A, A, None, None) == E_NULL
+    assert f(A, None, 1, 64, A, A, None, None) == E_NULL
+    assert f(A, A, 1, 64, None, A, None, None) == E_NULL
+    assert f(A, A, 1, 64, A, None, None, None) == E_NULL
+    assert f(A, A, 1, 64, A + 4, A, None, None) == E_UNSUP
+    assert f(A, A, 1, 64, A, A, A + 1, None) == E_UNSUP
+    assert f(None, None, 0, 64, None, None, None, None) == OK
+
+
+def test_index_score_validation(lib):
+    f = lib.lk_index_score
+    assert f(A, A, 64, A, A, 16, None, A, None) == E_NULL
+    assert f(A, A, 64, A, A, 16, rows(B=-1), A, None) == E_SHAPE
+    assert f(A, A, 64, A, A, 16, rows(T=17), A, None) == E_SHAPE             # T beyond the cache
+    assert f(A, A, 32, A, A, 16, rows(), A, None) == E_UNSUP                 # heads != 64
+    assert f(None, A, 64, A, A, 16, rows(), A, None) == E_NULL
+    assert f(A, A, 64, None, A, 16, rows(), A, None) == E_NULL
+    assert f(A, A, 64, A, A, 16, rows(), None, None) == E_NULL
+    assert f(A + 8, A, 64, A, A, 16, rows(), A, None) == E_UNSUP
+    assert f(A, A + 4, 64, A, A, 16, rows(), A, None) == E_UNSUP
+    assert f(A, A, 64, A, A, 16, rows(seq_len=A + 1), A, None) == E_UNSUP
+    assert f(A, A, 64, A, A, 70000, rows(B=70000, T=16), A, None) == E_UNSUP  # grid limit
+    assert f(None, None, 64, None, None, 16, rows(B=0), None, None) == OK
+    assert f(None, None, 64, None, None, 16, rows(T=0), None, None) == OK
+
+
+def test_topk_validation(lib):
+    f = lib.lk_topk
+    assert f(A, None, 8, A, None) == E_NULL
+    assert f(A, rows(), 0, A, None) == E_SHAPE
+    assert f(A, rows(S=-2), 8, A, None) == E_SHAPE
+    assert f(A, rows(T=16385), 8, A, None) == E_UNSUP
+    assert f(None, rows(), 8, A, None) == E_NULL
+    assert f(A, rows(), 8, None, None) == E_NULL
+    assert f(A + 2, rows(), 8, A, None) == E_UNSUP
+    assert f(None, rows(B=0), 8, None, None) == OK
+
+
+def test_python_binding_raises_without_gpu_tensors():
+    import torch
+    from sparse_attention_lightning_fp8_amd import api
+    with pytest.raises(ValueError):
+        api.lk_topk(torch.zeros(1, 1, 4, dtype=torch.float64), 2)
+    with pytest.raises(ValueError):
+        api.lk_quantize_queries(torch.zeros(2, 64, 128, dtype=torch.float32), torch.zeros(2, 64))

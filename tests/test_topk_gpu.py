@@ -1,0 +1,86 @@
+"""Per-row top-k on the GPU: exactly the oracle's set on the same float32 scores."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sparse_attention_lightning_fp8_amd import api
+from tests._parity import log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gpu_topk(scores: np.ndarray, k: int, lens=None, causal=False, start_pos=0):
+    s = torch.from_numpy(np.ascontiguousarray(scores, np.float32)).to(DEV)
+    sl = torch.from_numpy(np.asarray(lens, np.int32)).to(DEV) if lens is not None else None
+    idx = api.lk_topk(s, k, start_pos=start_pos, seq_len=sl, causal=causal)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+def _check_exact(scores, k, gidx, lens=None, causal=False, start_pos=0):
+    B, S, T = scores.shape
+    for b in range(B):
+        for t in range(S):
+            sl = max(int(lens[b]), 0) if lens is not None else -1
+            L = O.valid_len(T, sl, causal, start_pos, t)
+            want = O.topk(np.ascontiguousarray(scores[b, t], np.float32), L, k)
+            got = gidx[b, t]
+            assert sorted(got.tolist()) == sorted(want.tolist()), f"row ({b},{t}) L={L}"
+
+
+@pytest.mark.parametrize("T,k", [(1, 1), (5, 2), (1001, 256), (2049, 2048), (4096, 2048), (16384, 2048),
+                                 (16384, 1), (16384, 16384), (3000, 4000)])
+def test_topk_random_rows_exact(T, k):
+    rng = np.random.default_rng(T + k)
+    scores = rng.standard_normal((2, 3, T)).astype(np.float32)
+    log(f"[topk] random T={T} k={k}")
+    _check_exact(scores, k, _gpu_topk(scores, k), None)
+
+
+def test_topk_ties_signed_zeros_and_infinities():
+    rng = np.random.default_rng(5)
+    T = 5000
+    s = rng.integers(-4, 4, (3, 2, T)).astype(np.float32)      # heavy ties
+    s[0, 0, ::2] = -0.0
+    s[0, 0, 1::2] = 0.0
+    s[1, 1, :] = -np.inf
+    s[1, 1, 17] = 1.0
+    s[2, 0, :] = 3.0                                           # all equal
+    s[2, 1, 100:] = -np.inf
+    log("[topk] ties")
+    for k in (1, 7, 2048, 4999):
+        _check_exact(s, k, _gpu_topk(s, k), None)
+
+
+def test_topk_ragged_and_causal_rows():
+    rng = np.random.default_rng(6)
+    T = 3000
+    s = rng.standard_normal((4, 1, T)).astype(np.float32)
+    lens = [0, 1, 2048, 2500]
+    log("[topk] ragged")
+    _check_exact(s, 2048, _gpu_topk(s, 2048, lens=lens), lens=lens)
+    s2 = rng.standard_normal((2, 40, 2100)).astype(np.float32)
+    log("[topk] causal")
+    g = _gpu_topk(s2, 2048, causal=True, start_pos=2040)
+    _check_exact(s2, 2048, g, causal=True, start_pos=2040)
+
+
+def test_topk_deterministic_and_ordered():
+    rng = np.random.default_rng(7)
+    s = rng.integers(0, 50, (2, 2, 16384)).astype(np.float32)
+    log("[topk] determinism")
+    a = _gpu_topk(s, 2048)
+    b = _gpu_topk(s, 2048)
+    assert np.array_equal(a, b)
+    # documented order: strictly-greater indices ascending, then tied ones ascending
+    for bi in range(2):
+        for ti in range(2):
+            r = a[bi, ti]
+            v = s[bi, ti][r]
+            kth = v.min()
+            gt = r[v > kth]
+            eq = r[v == kth]
+            assert np.all(np.diff(gt) > 0) and np.all(np.diff(eq) > 0)
+            assert np.array_equal(r, np.concatenate([gt, eq]))
