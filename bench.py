@@ -1,0 +1,306 @@
+"""Benchmark of the lightning-indexer hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: key write of the step's new
+tokens, query rotate/quantize + weight fold, fp8 index score with mask, per-row top-k.
+The step rate comes from an uninstrumented timed loop; per-kernel durations come from a
+second pass of the same steps with events recorded at each dispatch's start and end.
+The timed workload is decode with 16 sequences of 16384 cached keys (64 heads x 128,
+top-2048); every input is resident in HBM before timing, and R copies of the inputs
+are rotated so the 256 MB last-level cache cannot serve the 33 MB key cache.
+
+Prints ONE JSON line.  Prefill (4096x4096 causal) and chunked prefill (2 x 4096 new
+tokens against 16384 keys) are timed too and reported under "extra".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode keys scored/s + HBM GB/s (B16,T16K); prefill index fp8 TFLOP/s"
+HBM_PEAK_GBPS = 8000.0
+F16_PEAK_TFLOPS = 2500.0      # dense f16 MFMA (the dtype the contraction runs in)
+FP8_PEAK_TFLOPS = 5000.0      # dense fp8 MFMA
+BYTES_PER_KEY = 136           # 128 B key + 4 B key scale + 4 B score
+BYTES_PER_QUERY_ROW = 64 * (128 + 4)
+FLOP_PER_PAIR = 2 * 64 * 128
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+SCORE_SRC = os.path.join(ROOT, "sparse_attention_lightning_fp8_amd", "csrc", "score.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=16, help="input copies cycled through to defeat the LLC")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------- setup
+class DecodeSet:
+    """One copy of every input and output of a decode step."""
+
+    def __init__(self, api, inp, cache, cache_scale, dev):
+        import torch
+        wl = inp.wl
+        self.cache = cache
+        self.cache_scale = cache_scale
+        self.k_new = torch.stack([inp.k[b, int(inp.positions[b]):int(inp.positions[b]) + wl.S]
+                                  for b in range(wl.B)]).to(dev)
+        self.positions = inp.positions.to(dev)
+        self.q = inp.q.to(dev)
+        self.w = inp.w.to(dev)
+        self.q8 = torch.empty(self.q.shape, dtype=torch.uint8, device=dev)
+        self.w_eff = torch.empty_like(self.w)
+        self.scores = torch.empty((wl.B, wl.S, wl.T), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((wl.B, wl.S, wl.k), dtype=torch.int32, device=dev)
+        self.seq_len = inp.lens.to(dev) if inp.lens is not None else None
+
+
+def make_sets(api, inp, n_sets, dev):
+    import torch
+    wl = inp.wl
+    cache = torch.zeros((wl.B, wl.cap, 128), dtype=torch.uint8, device=dev)
+    cache_scale = torch.zeros((wl.B, wl.cap), dtype=torch.float32, device=dev)
+    api.lk_quantize_keys(inp.k.to(dev), cache, cache_scale)      # the cached prefix (untimed)
+    sets = [DecodeSet(api, inp, cache, cache_scale, dev)]
+    for _ in range(n_sets - 1):
+        sets.append(DecodeSet(api, inp, cache.clone(), cache_scale.clone(), dev))
+    torch.cuda.synchronize()
+    return sets
+
+
+def raw_calls(wl, s):
+    """Pre-marshalled C-ABI calls of one step (the same entry points the Python binding
+    wraps, with the argument checks done once), so the host enqueues a step in a few
+    microseconds and the GPU, not Python, sets the pace of the timed loop."""
+    import ctypes
+    import torch
+    from sparse_attention_lightning_fp8_amd import _lib
+    lib = _lib.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    cap = s.cache.shape[1]
+    seq_len = s.seq_len.data_ptr() if s.seq_len is not None else None
+    s.rows = _lib.LkRows(wl.B, wl.S, wl.T, wl.start_pos, seq_len, 1 if wl.causal else 0)
+    rows = ctypes.byref(s.rows)
+    return [
+        (lib.lk_quantize_keys, (s.k_new.data_ptr(), wl.B, wl.S, s.k_new.stride(0) // 128, s.cache.data_ptr(),
+                                s.cache_scale.data_ptr(), cap, cap, 0, s.positions.data_ptr(), stream)),
+        (lib.lk_quantize_queries, (s.q.data_ptr(), s.w.data_ptr(), wl.B * wl.S, 64, s.q8.data_ptr(),
+                                   s.w_eff.data_ptr(), None, stream)),
+        (lib.lk_index_score, (s.q8.data_ptr(), s.w_eff.data_ptr(), 64, s.cache.data_ptr(), s.cache_scale.data_ptr(),
+                              cap, rows, s.scores.data_ptr(), stream)),
+        (lib.lk_topk, (s.scores.data_ptr(), rows, wl.k, s.idx.data_ptr(), stream)),
+    ]
+
+
+def run_step(calls, ev=None, arm=None):
+    """One pass of the hot path.  `ev` (optional) holds one (start, stop) event pair per
+    kernel, armed through lk_profile_next_launch so the runtime records them at the
+    kernel's own start and end."""
+    for j, (fn, args) in enumerate(calls):
+        if ev:
+            arm(ev[j][0].cuda_event, ev[j][1].cuda_event)
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"{fn.__name__} returned {st}")
+
+
+def make_event_pairs(n_steps, n_kernels):
+    import torch
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n_kernels)] for _ in range(n_steps)]
+    for step in evs:                      # create the HIP events (torch creates them on first record)
+        for a, b in step:
+            a.record()
+            b.record()
+    torch.cuda.synchronize()
+    return evs
+
+
+def time_workload(api, wl_name, steps, warmup, n_sets, dev):
+    """Warm up, then time `steps` uninstrumented steps (wall clock between two device
+    synchronizations: this gives the step rate), then run the same `steps` again with
+    dispatch events armed on every kernel (this gives each kernel's mean duration)."""
+    import torch
+    from sparse_attention_lightning_fp8_amd import _lib
+    from sparse_attention_lightning_fp8_amd import workloads as W
+    wl = W.WORKLOADS[wl_name]
+    inp = W.make_inputs(wl, seed=0)
+    sets = make_sets(api, inp, n_sets, dev)
+    calls = [raw_calls(wl, s) for s in sets]
+    arm = _lib.load().lk_profile_next_launch
+    for i in range(warmup):
+        run_step(calls[i % n_sets])
+    evs = make_event_pairs(steps, 4)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run_step(calls[i % n_sets])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for i in range(steps):
+        run_step(calls[i % n_sets], evs[i], arm)
+    torch.cuda.synchronize()
+    names = ["key_write", "query_quant", "index_score", "topk"]
+    per = {n: sum(e[j][0].elapsed_time(e[j][1]) for e in evs) / steps * 1e3 for j, n in enumerate(names)}
+    return wl, inp, wall, per
+
+
+def valid_pairs(wl, inp):
+    """Unmasked (query, key) pairs of one step: row (b, t) has
+    L = min(T, len_b, start_pos + t + 1 if causal) valid keys."""
+    tot = 0
+    for b in range(wl.B):
+        cap = min(wl.T, int(inp.lens[b])) if inp.lens is not None else wl.T
+        for t in range(wl.S):
+            L = min(cap, wl.start_pos + t + 1) if wl.causal else cap
+            tot += max(L, 0)
+    return tot
+
+
+# ---------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl_name):
+    """The oracle, single-threaded, on the same decode step (all 16 rows): key write of the
+    new rows, query quantize + fold, scores against every cached key, sort-based top-k.
+    Its cache prefix is quantized by the oracle itself beforehand (untimed)."""
+    import numpy as np
+    from oracle import oracle as O
+    from sparse_attention_lightning_fp8_amd import workloads as W
+    wl = W.WORKLOADS[wl_name]
+    inp = W.make_inputs(wl, seed=0)
+    prefix = []
+    for b in range(wl.B):
+        p0 = int(inp.positions[b])
+        prefix.append(O.quantize_rows(W.bf16_bits(inp.k[b, :p0])))
+    t0 = time.perf_counter()
+    for b in range(wl.B):
+        p0 = int(inp.positions[b])
+        kn, ksn = O.quantize_rows(W.bf16_bits(inp.k[b, p0:p0 + wl.S]))
+        k8 = np.concatenate([prefix[b][0], kn])
+        ks = np.concatenate([prefix[b][1], ksn])
+        for t in range(wl.S):
+            q8, qs = O.quantize_rows(W.bf16_bits(inp.q[b, t]))
+            w_eff = O.fold_weights(inp.w[b, t].numpy(), qs)
+            L = O.valid_len(wl.T, -1, wl.causal, wl.start_pos, t)
+            s = O.score_row(q8, w_eff, k8, ks, wl.T, L)
+            O.topk(s, L, wl.k)
+    dt = time.perf_counter() - t0
+    keys = wl.B * wl.S * wl.T
+    return {"value": keys / dt, "unit": "keys/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full {wl_name} step (B={wl.B}, T={wl.T}: key write, query quantize, "
+                      f"{keys} key scores, top-{wl.k}), single-threaded, {dt:.2f} s"}
+
+
+# ---------------------------------------------------------------------------- traffic
+def measured_traffic():
+    """HBM bytes per score launch from committed rocprofv3 PMC runs, if they were taken
+    on the current score kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        h = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
+        if rec.get("score_src_sha256") == h:
+            return rec["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+
+
+# ---------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the indexer shards by "
+              "sequence or query rows with no exchange, so per-GPU throughput is the single-GPU figure.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    from sparse_attention_lightning_fp8_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    from sparse_attention_lightning_fp8_amd import api
+    dev = "cuda:0"
+    torch.cuda.init()
+
+    log("decode_b16_t16384: setting up")
+    wl, inp, wall, per = time_workload(api, "decode_b16_t16384", args.steps, args.warmup, args.rotate, dev)
+    keys = wl.B * wl.S * wl.T
+    ms_step = wall / args.steps * 1e3
+    value = keys * args.steps / wall
+    score_bytes = keys * BYTES_PER_KEY + wl.B * wl.S * BYTES_PER_QUERY_ROW
+    score_us = per["index_score"]
+    achieved = score_bytes / (score_us * 1e-6) / 1e9
+    log(f"decode: {ms_step * 1e3:.1f} us/step, kernels {per}")
+
+    extra = {"score_kernel_us": score_us, "score_hbm_GBps": achieved,
+             "step_kernel_us": per, "keys_per_s_score_kernel": keys / (score_us * 1e-6)}
+    if not args.no_prefill:
+        for name in ("prefill_s4096", "chunked_prefill_b2_s4096"):
+            log(f"{name}: setting up")
+            pwl, pinp, pwall, pper = time_workload(api, name, args.prefill_steps, 2, 1, dev)
+            pairs = valid_pairs(pwl, pinp)
+            flops = pairs * FLOP_PER_PAIR
+            tf = flops / (pper["index_score"] * 1e-6) / 1e12
+            extra[name] = {"step_ms": pwall / args.prefill_steps * 1e3, "kernel_us": pper,
+                           "valid_pairs": pairs, "score_TFLOPs": tf,
+                           "score_frac_f16_peak": tf / F16_PEAK_TFLOPS, "score_frac_fp8_peak": tf / FP8_PEAK_TFLOPS}
+            log(f"{name}: score {pper['index_score']:.1f} us = {tf:.1f} TFLOP/s")
+            del pinp
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle): running")
+        cpu = cpu_baseline("decode_b16_t16384")
+        log(f"cpu baseline: {cpu['value']:.3e} keys/s")
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "keys/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 e4m3 operands, f16 MFMA, f32 accumulate", "data": "synthetic",
+        "config": {"workload": "decode_b16_t16384", "B": wl.B, "T": wl.T, "heads": 64, "dim": 128,
+                   "topk": wl.k, "rotated_input_copies": args.rotate},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
+                     "kernel": "score_decode_kernel", "algorithmic_bytes": score_bytes},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,8 @@
  *     enqueues nothing.  LK_E_HIP reports a failed kernel launch
  *     (hipGetLastError() after the launch).
  *   - bf16 data is passed as its uint16 bit pattern; fp8 data is e4m3fn bytes.
- *   - The library keeps no state, prints nothing and never aborts; calls are
+ *   - The library keeps no state (apart from the per-thread profiling events of
+ *     lk_profile_next_launch), prints nothing and never aborts; calls are
  *     thread-safe.  Non-finite inputs are outside the contract.
  *   - Zero-sized work (no rows, no keys) returns LK_OK and enqueues nothing.
  */
@@ -149,6 +150,17 @@ LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_
  */
 LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, int32_t *idx,
                          hipStream_t stream);
+
+/*
+ * Profiling aid, outside the indexer computation: arm two HIP events for the next
+ * kernel that the calling thread launches through an lk_* entry point.  The runtime
+ * records `start` when that kernel begins executing and `stop` when it ends
+ * (hipExtLaunchKernel), so hipEventElapsedTime(start, stop) is the kernel's own
+ * duration without queueing gaps.  The next lk_* call consumes the pair whether or
+ * not it launches a kernel.  Events are caller-owned (hipEventCreate); LK_E_NULL if
+ * either is NULL.  The armed pair is per thread; nothing else is kept.
+ */
+LK_API lk_status lk_profile_next_launch(hipEvent_t start, hipEvent_t stop);
 
 /* Human-readable name of a status code (static storage). */
 LK_API const char *lk_status_string(lk_status s);

@@ -17,7 +17,19 @@ hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const ui
 hipError_t launch_topk(const float *scores, const RowsDev &rows, int32_t k, int32_t *idx, hipStream_t stream);
 }  // namespace lk
 
+namespace lk {
+LaunchEvents &armed_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+}  // namespace lk
+
 namespace {
+
+// Every entry point consumes the armed profiling events, launched or not.
+struct DisarmOnExit {
+    ~DisarmOnExit() { lk::armed_events() = lk::LaunchEvents{}; }
+};
 
 constexpr int64_t kMaxGridX = 0x7FFFFFFFLL;
 constexpr int64_t kMaxGridYZ = 65535;
@@ -51,6 +63,7 @@ LK_API lk_status lk_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_ro
                                   uint8_t *cache, float *cache_scale, int64_t cache_seq_stride,
                                   int64_t cache_rows, int64_t row_offset, const int32_t *positions,
                                   hipStream_t stream) {
+    DisarmOnExit disarm;
     if (n_seq < 0 || n_rows < 0 || x_seq_stride < 0 || cache_seq_stride < 0 || cache_rows < 0)
         return LK_E_SHAPE;
     if (cache_rows > cache_seq_stride) return LK_E_SHAPE;
@@ -65,6 +78,7 @@ LK_API lk_status lk_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_ro
 
 LK_API lk_status lk_quantize_queries(const uint16_t *q, const float *w, int64_t n_tokens, int32_t heads,
                                      uint8_t *q_fp8, float *w_eff, float *q_scale, hipStream_t stream) {
+    DisarmOnExit disarm;
     if (n_tokens < 0 || heads < 1) return LK_E_SHAPE;
     if (n_tokens == 0) return LK_OK;
     if (!q || !w || !q_fp8 || !w_eff) return LK_E_NULL;
@@ -79,6 +93,7 @@ LK_API lk_status lk_quantize_queries(const uint16_t *q, const float *w, int64_t 
 LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_t heads,
                                 const uint8_t *k_cache, const float *k_scale, int64_t cache_seq_stride,
                                 const lk_rows *rows, float *scores, hipStream_t stream) {
+    DisarmOnExit disarm;
     lk_status st = check_rows(rows);
     if (st != LK_OK) return st;
     if (cache_seq_stride < 0 || rows->T > cache_seq_stride) return LK_E_SHAPE;
@@ -95,6 +110,7 @@ LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_
 }
 
 LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, int32_t *idx, hipStream_t stream) {
+    DisarmOnExit disarm;
     lk_status st = check_rows(rows);
     if (st != LK_OK) return st;
     if (k < 1) return LK_E_SHAPE;
@@ -104,6 +120,12 @@ LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, in
     if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(rows->seq_len, 4)) return LK_E_UNSUPPORTED;
     if ((int64_t)rows->B * rows->S > kMaxGridX) return LK_E_UNSUPPORTED;
     return from_hip(lk::launch_topk(scores, to_dev(*rows), k, idx, stream));
+}
+
+LK_API lk_status lk_profile_next_launch(hipEvent_t start, hipEvent_t stop) {
+    if (!start || !stop) return LK_E_NULL;
+    lk::armed_events() = lk::LaunchEvents{start, stop};
+    return LK_OK;
 }
 
 LK_API const char *lk_status_string(lk_status s) {

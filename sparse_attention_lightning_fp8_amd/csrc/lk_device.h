@@ -1,6 +1,7 @@
 // lk_device.h -- device-side helpers shared by the gfx950 kernels of liblk.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -60,6 +61,26 @@ __device__ __forceinline__ half8 fp8x8_to_half8(uint32_t a, uint32_t b) {
 __device__ __forceinline__ float halves_sum_pair(float x, float y) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Events armed by lk_profile_next_launch for the calling thread's next launch.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents &armed_events();
+
+// Launch on `stream`; if events are armed, they are recorded at the kernel's own start
+// and end (hipExtLaunchKernel) and disarmed.  Returns the launch status.
+template <typename F, typename... Args>
+hipError_t launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t stream, Args... args) {
+    LaunchEvents &ev = armed_events();
+    if (ev.start && ev.stop) {
+        hipExtLaunchKernelGGL(kernel, grid, block, shm, stream, ev.start, ev.stop, 0u, args...);
+        ev = LaunchEvents{};
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, shm, stream, args...);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace lk

@@ -169,17 +169,15 @@ hipError_t launch_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_rows
                                 hipStream_t stream) {
     const int64_t total = n_seq * n_rows;
     const int64_t blocks = (total + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL(quantize_keys_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n_seq, n_rows,
+    return launch(quantize_keys_kernel, dim3((unsigned)blocks), dim3(256), 0u, stream, x, n_seq, n_rows,
                        x_seq_stride, cache, cache_scale, cache_seq_stride, cache_rows, row_offset, positions);
-    return hipGetLastError();
 }
 
 hipError_t launch_quantize_queries(const uint16_t *q, const float *w, int64_t n_rows, uint8_t *q_fp8,
                                    float *w_eff, float *q_scale, hipStream_t stream) {
     const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL(quantize_queries_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, w, n_rows,
+    return launch(quantize_queries_kernel, dim3((unsigned)blocks), dim3(256), 0u, stream, q, w, n_rows,
                        q_fp8, w_eff, q_scale);
-    return hipGetLastError();
 }
 
 }  // namespace lk

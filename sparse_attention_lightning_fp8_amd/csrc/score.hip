@@ -24,52 +24,91 @@ namespace lk {
 namespace {
 
 // Per-lane A operand (64 heads x 128 features of one query token) as f16, and the
-// matching folded weights: A[m][kk] is the K-step kk operand of M-tile m.
+// matching folded weights: a[m][kk] is the K-step kk operand of M-tile m.
 struct QueryFrag {
     half8 a[2][8];
     float w[2][16];
 };
 
-__device__ __forceinline__ void load_query(const uint8_t *__restrict__ q_row /*64 x 128*/,
-                                           const float *__restrict__ w_row /*64*/, int lane,
-                                           QueryFrag &f) {
+struct QueryRaw {          // the same data before conversion (issued as early loads)
+    uint4 q[2][4];
+    float4 w[2][4];
+};
+
+__device__ __forceinline__ void load_query_raw(const uint8_t *__restrict__ q_row /*64 x 128*/,
+                                               const float *__restrict__ w_row /*64*/, int lane,
+                                               QueryRaw &raw) {
     const int r = lane & 31, hh = lane >> 5;
 #pragma unroll
     for (int m = 0; m < 2; m++) {
         const uint4 *src = reinterpret_cast<const uint4 *>(q_row + (32 * m + r) * LK_DIM + 64 * hh);
-        uint4 v[4];
 #pragma unroll
-        for (int c = 0; c < 4; c++) v[c] = src[c];
+        for (int c = 0; c < 4; c++) raw.q[m][c] = src[c];
+#pragma unroll
+        for (int g = 0; g < 4; g++) raw.w[m][g] = *reinterpret_cast<const float4 *>(w_row + 32 * m + 8 * g + 4 * hh);
+    }
+}
+
+__device__ __forceinline__ void convert_query(const QueryRaw &raw, QueryFrag &f) {
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
 #pragma unroll
         for (int c = 0; c < 4; c++) {
-            f.a[m][2 * c] = fp8x8_to_half8(v[c].x, v[c].y);
-            f.a[m][2 * c + 1] = fp8x8_to_half8(v[c].z, v[c].w);
+            f.a[m][2 * c] = fp8x8_to_half8(raw.q[m][c].x, raw.q[m][c].y);
+            f.a[m][2 * c + 1] = fp8x8_to_half8(raw.q[m][c].z, raw.q[m][c].w);
         }
 #pragma unroll
         for (int g = 0; g < 4; g++) {
-            const float4 wv = *reinterpret_cast<const float4 *>(w_row + 32 * m + 8 * g + 4 * hh);
-            f.w[m][4 * g + 0] = wv.x;
-            f.w[m][4 * g + 1] = wv.y;
-            f.w[m][4 * g + 2] = wv.z;
-            f.w[m][4 * g + 3] = wv.w;
+            f.w[m][4 * g + 0] = raw.w[m][g].x;
+            f.w[m][4 * g + 1] = raw.w[m][g].y;
+            f.w[m][4 * g + 2] = raw.w[m][g].z;
+            f.w[m][4 * g + 3] = raw.w[m][g].w;
         }
     }
 }
 
+__device__ __forceinline__ void load_query(const uint8_t *__restrict__ q_row, const float *__restrict__ w_row,
+                                           int lane, QueryFrag &f) {
+    QueryRaw raw;
+    load_query_raw(q_row, w_row, lane, raw);
+    convert_query(raw, f);
+}
+
 // Head-weighted ReLU sum of the two M-tile accumulators (this lane's 32 heads).
+// Scores are finite by contract, so ReLU is a single v_max (the file is built
+// without NaN semantics).
 __device__ __forceinline__ float relu_weighted_sum(const float16v acc[2], const QueryFrag &f) {
     float s = 0.0f;
 #pragma unroll
     for (int m = 0; m < 2; m++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) s += __builtin_fmaxf(acc[m][i], 0.0f) * f.w[m][i];
+        for (int i = 0; i < 16; i++) s = __builtin_fmaf(__builtin_fmaxf(acc[m][i], 0.0f), f.w[m][i], s);
     return s;
+}
+
+// Scores of one 32-key tile whose B operand (this lane's 64 bytes of key l % 32) is `kv`.
+__device__ __forceinline__ float score_tile(const uint4 kv[4], const QueryFrag &f) {
+    float16v acc[2] = {};
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        const half8 b0 = fp8x8_to_half8(kv[c].x, kv[c].y);
+        const half8 b1 = fp8x8_to_half8(kv[c].z, kv[c].w);
+#pragma unroll
+        for (int m = 0; m < 2; m++) {
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][2 * c], b0, acc[m], 0, 0, 0);
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][2 * c + 1], b1, acc[m], 0, 0, 0);
+        }
+    }
+    return relu_weighted_sum(acc, f);
 }
 
 // ------------------------------------------------------------------ decode (S == 1)
 // One wave scores 128 consecutive keys (4 tiles of 32) of one query row; a block of
 // 4 waves covers 512 keys.  Each lane loads its 4 x 64 bytes of K straight into the
 // B-operand registers (keys are read exactly once, so LDS brings no reuse here).
+// Order of work: the small query/weight loads first (L2 hits), then every K load of
+// the wave (16 KB in flight), then the query conversion while K streams in, then the
+// tiles in arrival order, so compute overlaps the HBM stream.
 constexpr int kDecWaves = 4;
 constexpr int kDecTiles = 4;                       // 32-key tiles per wave
 constexpr int kDecKeysPerWave = 32 * kDecTiles;    // 128
@@ -81,7 +120,7 @@ score_decode_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict__
                     int64_t cache_seq_stride, RowsDev rows, float *__restrict__ scores) {
     const int lane = __lane_id();
     const int wave = threadIdx.x >> 6;
-    const int qrow = blockIdx.y;                       // b * S + t
+    const int qrow = blockIdx.y;                       // b * S + t  (S == 1)
     const int b = qrow / rows.S;
     const int t = qrow - b * rows.S;
     const int64_t T = rows.T;
@@ -98,50 +137,34 @@ score_decode_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict__
         return;
     }
     const int r = lane & 31, hh = lane >> 5;
+    QueryRaw raw;
+    load_query_raw(q_fp8 + (int64_t)qrow * LK_HEADS * LK_DIM, w_eff + (int64_t)qrow * LK_HEADS, lane, raw);
     const uint8_t *kbase = k_cache + (int64_t)b * cache_seq_stride * LK_DIM;
-    // Issue the K loads first (the long-latency HBM stream), then Q and w.
     uint4 kv[kDecTiles][4];
 #pragma unroll
     for (int j = 0; j < kDecTiles; j++) {
         const int64_t s = key0 + 32 * j + r;
-        if (s < L) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(kbase + s * LK_DIM + 64 * hh);
+        const uint4 *src = reinterpret_cast<const uint4 *>(kbase + (s < L ? s : 0) * LK_DIM + 64 * hh);
 #pragma unroll
-            for (int c = 0; c < 4; c++) kv[j][c] = src[c];
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; c++) kv[j][c] = make_uint4(0, 0, 0, 0);
-        }
+        for (int c = 0; c < 4; c++) kv[j][c] = src[c];       // rows past L re-read row 0 (masked below)
     }
     float ks[kDecTiles / 2];
 #pragma unroll
     for (int p = 0; p < kDecTiles / 2; p++) {
         const int64_t s = key0 + 64 * p + lane;
-        ks[p] = s < L ? k_scale[(int64_t)b * cache_seq_stride + s] : 0.0f;
+        ks[p] = k_scale[(int64_t)b * cache_seq_stride + (s < L ? s : 0)];
     }
+    // Keep every load above this point: all of the wave's K bytes must be in flight
+    // before any compute, or the stream stalls behind the MFMA work.
+    __builtin_amdgcn_sched_barrier(0);
     QueryFrag f;
-    load_query(q_fp8 + (int64_t)qrow * LK_HEADS * LK_DIM, w_eff + (int64_t)qrow * LK_HEADS, lane, f);
-
-    float part[kDecTiles];
-#pragma unroll
-    for (int j = 0; j < kDecTiles; j++) {
-        float16v acc[2] = {};
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const half8 b0 = fp8x8_to_half8(kv[j][c].x, kv[j][c].y);
-            const half8 b1 = fp8x8_to_half8(kv[j][c].z, kv[j][c].w);
-#pragma unroll
-            for (int m = 0; m < 2; m++) {
-                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][2 * c], b0, acc[m], 0, 0, 0);
-                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][2 * c + 1], b1, acc[m], 0, 0, 0);
-            }
-        }
-        part[j] = relu_weighted_sum(acc, f);
-    }
+    convert_query(raw, f);
 #pragma unroll
     for (int p = 0; p < kDecTiles / 2; p++) {
+        const float p0 = score_tile(kv[2 * p], f);
+        const float p1 = score_tile(kv[2 * p + 1], f);
         // lanes 0-31: tile 2p, key l; lanes 32-63: tile 2p+1, key l-32  ->  key key0 + 64p + l
-        const float sum = halves_sum_pair(part[2 * p], part[2 * p + 1]);
+        const float sum = halves_sum_pair(p0, p1);
         const int64_t s = key0 + 64 * p + lane;
         if (s < T) out[s] = s < L ? sum * ks[p] : -__builtin_inff();
     }
@@ -244,15 +267,14 @@ hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const ui
                               float *scores, hipStream_t stream) {
     if (rows.S == 1) {
         dim3 grid((unsigned)((rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock), (unsigned)rows.B);
-        hipLaunchKernelGGL(score_decode_kernel, grid, dim3(64 * kDecWaves), 0, stream, q_fp8, w_eff, k_cache,
-                           k_scale, cache_seq_stride, rows, scores);
+        return launch(score_decode_kernel, grid, dim3(64 * kDecWaves), 0u, stream, q_fp8, w_eff, k_cache,
+                      k_scale, cache_seq_stride, rows, scores);
     } else {
         dim3 grid((unsigned)((rows.T + kPreChunk - 1) / kPreChunk), (unsigned)((rows.S + kPreWaves - 1) / kPreWaves),
                   (unsigned)rows.B);
-        hipLaunchKernelGGL(score_prefill_kernel, grid, dim3(64 * kPreWaves), 0, stream, q_fp8, w_eff, k_cache,
-                           k_scale, cache_seq_stride, rows, scores);
+        return launch(score_prefill_kernel, grid, dim3(64 * kPreWaves), 0u, stream, q_fp8, w_eff, k_cache,
+                      k_scale, cache_seq_stride, rows, scores);
     }
-    return hipGetLastError();
 }
 
 }  // namespace lk

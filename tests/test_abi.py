@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     assert syms == sorted(["lk_quantize_keys", "lk_quantize_queries", "lk_index_score", "lk_topk",
-                           "lk_status_string", "lk_abi_version"])
+                           "lk_profile_next_launch", "lk_status_string", "lk_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -101,6 +101,14 @@ def test_topk_validation(lib):
     assert f(A, rows(), 8, None, None) == E_NULL
     assert f(A + 2, rows(), 8, A, None) == E_UNSUP
     assert f(None, rows(B=0), 8, None, None) == OK
+
+
+def test_profile_next_launch_validation(lib):
+    assert lib.lk_profile_next_launch(None, A) == E_NULL
+    assert lib.lk_profile_next_launch(A, None) == E_NULL
+    # arming fake handles and then failing validation consumes them without any HIP call
+    assert lib.lk_profile_next_launch(A, A) == OK
+    assert lib.lk_topk(A, rows(), 0, A, None) == E_SHAPE
 
 
 def test_python_binding_raises_without_gpu_tensors():
