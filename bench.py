@@ -101,10 +101,10 @@ def raw_calls(wl, s):
     s.rows = _lib.LkRows(wl.B, wl.S, wl.T, wl.start_pos, seq_len, 1 if wl.causal else 0)
     rows = ctypes.byref(s.rows)
     return [
-        (lib.lk_quantize_keys, (s.k_new.data_ptr(), wl.B, wl.S, s.k_new.stride(0) // 128, s.cache.data_ptr(),
-                                s.cache_scale.data_ptr(), cap, cap, 0, s.positions.data_ptr(), stream)),
-        (lib.lk_quantize_queries, (s.q.data_ptr(), s.w.data_ptr(), wl.B * wl.S, 64, s.q8.data_ptr(),
-                                   s.w_eff.data_ptr(), None, stream)),
+        (lib.lk_prepare, (s.k_new.data_ptr(), wl.B, wl.S, s.k_new.stride(0) // 128, s.cache.data_ptr(),
+                          s.cache_scale.data_ptr(), cap, cap, 0, s.positions.data_ptr(),
+                          s.q.data_ptr(), s.w.data_ptr(), wl.B * wl.S, 64, s.q8.data_ptr(),
+                          s.w_eff.data_ptr(), None, stream)),
         (lib.lk_index_score, (s.q8.data_ptr(), s.w_eff.data_ptr(), 64, s.cache.data_ptr(), s.cache_scale.data_ptr(),
                               cap, rows, s.scores.data_ptr(), stream)),
         (lib.lk_topk, (s.scores.data_ptr(), rows, wl.k, s.idx.data_ptr(), stream)),
@@ -112,7 +112,8 @@ def raw_calls(wl, s):
 
 
 def run_step(calls, ev=None, arm=None):
-    """One pass of the hot path.  `ev` (optional) holds one (start, stop) event pair per
+    """One pass of the hot path (lk_prepare: key write + query quantize and weight fold;
+    lk_index_score; lk_topk).  `ev` (optional) holds one (start, stop) event pair per
     kernel, armed through lk_profile_next_launch so the runtime records them at the
     kernel's own start and end."""
     for j, (fn, args) in enumerate(calls):
@@ -149,7 +150,7 @@ def time_workload(api, wl_name, steps, warmup, n_sets, dev):
     arm = _lib.load().lk_profile_next_launch
     for i in range(warmup):
         run_step(calls[i % n_sets])
-    evs = make_event_pairs(steps, 4)
+    evs = make_event_pairs(steps, 3)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -159,7 +160,7 @@ def time_workload(api, wl_name, steps, warmup, n_sets, dev):
     for i in range(steps):
         run_step(calls[i % n_sets], evs[i], arm)
     torch.cuda.synchronize()
-    names = ["key_write", "query_quant", "index_score", "topk"]
+    names = ["prepare", "index_score", "topk"]
     per = {n: sum(e[j][0].elapsed_time(e[j][1]) for e in evs) / steps * 1e3 for j, n in enumerate(names)}
     return wl, inp, wall, per
 

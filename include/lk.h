@@ -118,6 +118,18 @@ LK_API lk_status lk_quantize_queries(const uint16_t *q, const float *w, int64_t 
                                      float *q_scale, hipStream_t stream);
 
 /*
+ * lk_quantize_keys and lk_quantize_queries in ONE kernel launch: the key write of
+ * a step's new tokens and the query preparation are independent, and a decode step
+ * is short enough that a second launch costs more than either job.  Arguments,
+ * results and errors are exactly those of the two calls (either job may be empty).
+ */
+LK_API lk_status lk_prepare(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride,
+                            uint8_t *cache, float *cache_scale, int64_t cache_seq_stride,
+                            int64_t cache_rows, int64_t row_offset, const int32_t *positions,
+                            const uint16_t *q, const float *w, int64_t n_tokens, int32_t heads,
+                            uint8_t *q_fp8, float *w_eff, float *q_scale, hipStream_t stream);
+
+/*
  * fp8_index + mask (page "Index scores"): for every valid (b, t, s)
  *   scores[(b*S + t)*T + s] = k_scale[b*cache_seq_stride + s]
  *        * sum_h w_eff[(b*S + t)*heads + h] * ReLU( q8[(b*S+t), h, :] . k8[b, s, :] )

@@ -27,6 +27,8 @@ class LkRows(ctypes.Structure):
 SIGNATURES = {
     "lk_quantize_keys": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _i64, _i64, _p, _p]),
     "lk_quantize_queries": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p, _p, _p]),
+    "lk_prepare": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _i64, _i64, _p,
+                                  _p, _p, _i64, _i32, _p, _p, _p, _p]),
     "lk_index_score": (ctypes.c_int, [_p, _p, _i32, _p, _p, _i64, ctypes.POINTER(LkRows), _p, _p]),
     "lk_topk": (ctypes.c_int, [_p, ctypes.POINTER(LkRows), _i32, _p, _p]),
     "lk_profile_next_launch": (ctypes.c_int, [_p, _p]),

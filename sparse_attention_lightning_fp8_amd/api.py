@@ -41,11 +41,7 @@ def _rows(B: int, S: int, T: int, start_pos: int, seq_len: Optional[torch.Tensor
     return LkRows(B, S, T, start_pos, ptr, 1 if causal else 0)
 
 
-def lk_quantize_keys(x: torch.Tensor, cache: torch.Tensor, cache_scale: torch.Tensor,
-                     row_offset: int = 0, positions: Optional[torch.Tensor] = None) -> None:
-    """Rotate + quantize x [n_seq, n_rows, 128] (bf16) into cache [N, cap, 128] (uint8 or
-    float8_e4m3fn) and cache_scale [N, cap] or [N, cap, 1] (float32), rows starting at
-    `row_offset` or at positions[b] (int32 CUDA [n_seq])."""
+def _key_args(x, cache, cache_scale, row_offset, positions):
     _need(x.dtype == torch.bfloat16 and x.dim() == 3 and x.shape[2] == DIM, "x must be bf16 [n_seq, n_rows, 128]")
     _need(x.stride(2) == 1 and x.stride(1) == DIM and x.stride(0) % DIM == 0, "x rows must be contiguous")
     cache = _byte_view(cache)
@@ -64,16 +60,11 @@ def lk_quantize_keys(x: torch.Tensor, cache: torch.Tensor, cache_scale: torch.Te
         _need(positions.dtype == torch.int32 and positions.is_cuda and positions.is_contiguous()
               and positions.numel() >= x.shape[0], "positions must be int32 CUDA [n_seq]")
         pos_ptr = positions.data_ptr()
-    st = _lib.load().lk_quantize_keys(x.data_ptr(), x.shape[0], x.shape[1], x.stride(0) // DIM,
-                                      cache.data_ptr(), cs.data_ptr(), seq_stride, cache.shape[1],
-                                      row_offset, pos_ptr, _stream(x))
-    _lib.check("lk_quantize_keys", st)
+    return (x.data_ptr(), x.shape[0], x.shape[1], x.stride(0) // DIM, cache.data_ptr(), cs.data_ptr(),
+            seq_stride, cache.shape[1], row_offset, pos_ptr)
 
 
-def lk_quantize_queries(q: torch.Tensor, w: torch.Tensor, q_fp8: Optional[torch.Tensor] = None,
-                        w_eff: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None):
-    """q [..., H, 128] bf16 and w [..., H] float32 -> (q_fp8 uint8 [..., H, 128], w_eff float32 [..., H]).
-    If `q_scale` (float32 [..., H]) is given it receives the per-head scales."""
+def _query_args(q, w, q_fp8, w_eff, q_scale):
     _need(q.dtype == torch.bfloat16 and q.shape[-1] == DIM and q.is_contiguous(), "q must be contiguous bf16 [..., H, 128]")
     _need(w.dtype == torch.float32 and w.shape == q.shape[:-1] and w.is_contiguous(), "w must be contiguous float32 [..., H]")
     H = q.shape[-2]
@@ -89,9 +80,36 @@ def lk_quantize_queries(q: torch.Tensor, w: torch.Tensor, q_fp8: Optional[torch.
     if q_scale is not None:
         _need(q_scale.dtype == torch.float32 and q_scale.shape == w.shape and q_scale.is_contiguous(), "bad q_scale")
         qs_ptr = q_scale.data_ptr()
-    st = _lib.load().lk_quantize_queries(q.data_ptr(), w.data_ptr(), n_tok, H, q8.data_ptr(),
-                                         w_eff.data_ptr(), qs_ptr, _stream(q))
-    _lib.check("lk_quantize_queries", st)
+    return (q.data_ptr(), w.data_ptr(), n_tok, H, q8.data_ptr(), w_eff.data_ptr(), qs_ptr), q_fp8, w_eff
+
+
+def lk_quantize_keys(x: torch.Tensor, cache: torch.Tensor, cache_scale: torch.Tensor,
+                     row_offset: int = 0, positions: Optional[torch.Tensor] = None) -> None:
+    """Rotate + quantize x [n_seq, n_rows, 128] (bf16) into cache [N, cap, 128] (uint8 or
+    float8_e4m3fn) and cache_scale [N, cap] or [N, cap, 1] (float32), rows starting at
+    `row_offset` or at positions[b] (int32 CUDA [n_seq])."""
+    args = _key_args(x, cache, cache_scale, row_offset, positions)
+    _lib.check("lk_quantize_keys", _lib.load().lk_quantize_keys(*args, _stream(x)))
+
+
+def lk_quantize_queries(q: torch.Tensor, w: torch.Tensor, q_fp8: Optional[torch.Tensor] = None,
+                        w_eff: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None):
+    """q [..., H, 128] bf16 and w [..., H] float32 -> (q_fp8 uint8 [..., H, 128], w_eff float32 [..., H]).
+    If `q_scale` (float32 [..., H]) is given it receives the per-head scales."""
+    args, q_fp8, w_eff = _query_args(q, w, q_fp8, w_eff, q_scale)
+    _lib.check("lk_quantize_queries", _lib.load().lk_quantize_queries(*args, _stream(q)))
+    return q_fp8, w_eff
+
+
+def lk_prepare(x: torch.Tensor, cache: torch.Tensor, cache_scale: torch.Tensor, q: torch.Tensor,
+               w: torch.Tensor, row_offset: int = 0, positions: Optional[torch.Tensor] = None,
+               q_fp8: Optional[torch.Tensor] = None, w_eff: Optional[torch.Tensor] = None,
+               q_scale: Optional[torch.Tensor] = None):
+    """lk_quantize_keys + lk_quantize_queries in one kernel launch; returns (q_fp8, w_eff)."""
+    kargs = _key_args(x, cache, cache_scale, row_offset, positions)
+    qargs, q_fp8, w_eff = _query_args(q, w, q_fp8, w_eff, q_scale)
+    _need(q.device == x.device, "tensors must be on one CUDA device")
+    _lib.check("lk_prepare", _lib.load().lk_prepare(*kargs, *qargs, _stream(x)))
     return q_fp8, w_eff
 
 

@@ -5,12 +5,7 @@
 #include "lk_device.h"
 
 namespace lk {
-hipError_t launch_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride,
-                                uint8_t *cache, float *cache_scale, int64_t cache_seq_stride,
-                                int64_t cache_rows, int64_t row_offset, const int32_t *positions,
-                                hipStream_t stream);
-hipError_t launch_quantize_queries(const uint16_t *q, const float *w, int64_t n_rows, uint8_t *q_fp8,
-                                   float *w_eff, float *q_scale, hipStream_t stream);
+hipError_t launch_quantize(const KeyJobArgs &ka, const QueryJobArgs &qa, hipStream_t stream);
 hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
                               const float *k_scale, int64_t cache_seq_stride, const RowsDev &rows,
                               float *scores, hipStream_t stream);
@@ -59,11 +54,14 @@ lk::RowsDev to_dev(const lk_rows &r) {
 
 extern "C" {
 
-LK_API lk_status lk_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride,
-                                  uint8_t *cache, float *cache_scale, int64_t cache_seq_stride,
-                                  int64_t cache_rows, int64_t row_offset, const int32_t *positions,
-                                  hipStream_t stream) {
-    DisarmOnExit disarm;
+}  // extern "C"
+
+namespace {
+
+// Validate a key-write request and fill `a` (n_seq == 0 or n_rows == 0: empty job).
+lk_status check_keys(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride, uint8_t *cache,
+                     float *cache_scale, int64_t cache_seq_stride, int64_t cache_rows, int64_t row_offset,
+                     const int32_t *positions, lk::KeyJobArgs &a) {
     if (n_seq < 0 || n_rows < 0 || x_seq_stride < 0 || cache_seq_stride < 0 || cache_rows < 0)
         return LK_E_SHAPE;
     if (cache_rows > cache_seq_stride) return LK_E_SHAPE;
@@ -71,14 +69,15 @@ LK_API lk_status lk_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_ro
     if (!x || !cache || !cache_scale) return LK_E_NULL;
     if (!aligned(x, 16) || !aligned(cache, 16) || !aligned(cache_scale, 4) || !aligned(positions, 4))
         return LK_E_UNSUPPORTED;
-    if (n_rows > INT64_MAX / n_seq || (n_seq * n_rows + 31) / 32 > kMaxGridX) return LK_E_UNSUPPORTED;
-    return from_hip(lk::launch_quantize_keys(x, n_seq, n_rows, x_seq_stride, cache, cache_scale,
-                                             cache_seq_stride, cache_rows, row_offset, positions, stream));
+    if (n_rows > INT64_MAX / n_seq || (n_seq * n_rows + 31) / 32 > kMaxGridX / 2) return LK_E_UNSUPPORTED;
+    a = lk::KeyJobArgs{x, n_seq, n_rows, x_seq_stride, cache, cache_scale, cache_seq_stride, cache_rows,
+                       row_offset, positions};
+    return LK_OK;
 }
 
-LK_API lk_status lk_quantize_queries(const uint16_t *q, const float *w, int64_t n_tokens, int32_t heads,
-                                     uint8_t *q_fp8, float *w_eff, float *q_scale, hipStream_t stream) {
-    DisarmOnExit disarm;
+// Validate a query request and fill `a` (n_tokens == 0: empty job).
+lk_status check_queries(const uint16_t *q, const float *w, int64_t n_tokens, int32_t heads, uint8_t *q_fp8,
+                        float *w_eff, float *q_scale, lk::QueryJobArgs &a) {
     if (n_tokens < 0 || heads < 1) return LK_E_SHAPE;
     if (n_tokens == 0) return LK_OK;
     if (!q || !w || !q_fp8 || !w_eff) return LK_E_NULL;
@@ -86,8 +85,55 @@ LK_API lk_status lk_quantize_queries(const uint16_t *q, const float *w, int64_t 
         return LK_E_UNSUPPORTED;
     if (n_tokens > INT64_MAX / heads) return LK_E_UNSUPPORTED;
     const int64_t n_rows = n_tokens * heads;
-    if ((n_rows + 31) / 32 > kMaxGridX) return LK_E_UNSUPPORTED;
-    return from_hip(lk::launch_quantize_queries(q, w, n_rows, q_fp8, w_eff, q_scale, stream));
+    if ((n_rows + 31) / 32 > kMaxGridX / 2) return LK_E_UNSUPPORTED;
+    a = lk::QueryJobArgs{q, w, n_rows, q_fp8, w_eff, q_scale};
+    return LK_OK;
+}
+
+lk_status run_quantize(const lk::KeyJobArgs &ka, const lk::QueryJobArgs &qa, hipStream_t stream) {
+    if (ka.n_seq * ka.n_rows == 0 && qa.n_rows == 0) return LK_OK;
+    return from_hip(lk::launch_quantize(ka, qa, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+LK_API lk_status lk_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride,
+                                  uint8_t *cache, float *cache_scale, int64_t cache_seq_stride,
+                                  int64_t cache_rows, int64_t row_offset, const int32_t *positions,
+                                  hipStream_t stream) {
+    DisarmOnExit disarm;
+    lk::KeyJobArgs ka;
+    lk_status st = check_keys(x, n_seq, n_rows, x_seq_stride, cache, cache_scale, cache_seq_stride, cache_rows,
+                              row_offset, positions, ka);
+    if (st != LK_OK) return st;
+    return run_quantize(ka, lk::QueryJobArgs{}, stream);
+}
+
+LK_API lk_status lk_quantize_queries(const uint16_t *q, const float *w, int64_t n_tokens, int32_t heads,
+                                     uint8_t *q_fp8, float *w_eff, float *q_scale, hipStream_t stream) {
+    DisarmOnExit disarm;
+    lk::QueryJobArgs qa;
+    lk_status st = check_queries(q, w, n_tokens, heads, q_fp8, w_eff, q_scale, qa);
+    if (st != LK_OK) return st;
+    return run_quantize(lk::KeyJobArgs{}, qa, stream);
+}
+
+LK_API lk_status lk_prepare(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride,
+                            uint8_t *cache, float *cache_scale, int64_t cache_seq_stride, int64_t cache_rows,
+                            int64_t row_offset, const int32_t *positions, const uint16_t *q, const float *w,
+                            int64_t n_tokens, int32_t heads, uint8_t *q_fp8, float *w_eff, float *q_scale,
+                            hipStream_t stream) {
+    DisarmOnExit disarm;
+    lk::KeyJobArgs ka;
+    lk::QueryJobArgs qa;
+    lk_status st = check_keys(x, n_seq, n_rows, x_seq_stride, cache, cache_scale, cache_seq_stride, cache_rows,
+                              row_offset, positions, ka);
+    if (st != LK_OK) return st;
+    st = check_queries(q, w, n_tokens, heads, q_fp8, w_eff, q_scale, qa);
+    if (st != LK_OK) return st;
+    return run_quantize(ka, qa, stream);
 }
 
 LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_t heads,

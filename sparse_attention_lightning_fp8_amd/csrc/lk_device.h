@@ -63,6 +63,23 @@ __device__ __forceinline__ float halves_sum_pair(float x, float y) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Arguments of the two quantization jobs (keys into the cache; queries + weight fold).
+struct KeyJobArgs {
+    const uint16_t *x = nullptr;
+    int64_t n_seq = 0, n_rows = 0, x_seq_stride = 0;
+    uint8_t *cache = nullptr;
+    float *cache_scale = nullptr;
+    int64_t cache_seq_stride = 0, cache_rows = 0, row_offset = 0;
+    const int32_t *positions = nullptr;
+};
+struct QueryJobArgs {
+    const uint16_t *q = nullptr;
+    const float *w = nullptr;
+    int64_t n_rows = 0;
+    uint8_t *q_fp8 = nullptr;
+    float *w_eff = nullptr, *q_scale = nullptr;
+};
+
 // Events armed by lk_profile_next_launch for the calling thread's next launch.
 struct LaunchEvents {
     hipEvent_t start = nullptr, stop = nullptr;

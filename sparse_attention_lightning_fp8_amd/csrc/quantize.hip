@@ -113,71 +113,82 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
     }
 }
 
-__global__ void __launch_bounds__(256)
-quantize_keys_kernel(const uint16_t *__restrict__ x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride,
-                     uint8_t *__restrict__ cache, float *__restrict__ cache_scale,
-                     int64_t cache_seq_stride, int64_t cache_rows, int64_t row_offset,
-                     const int32_t *__restrict__ positions) {
-    const int64_t g = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 3);
-    const int sub = threadIdx.x & 7;
-    const int64_t total = n_seq * n_rows;
-    // Keep all 8 lanes of a row together: rows past the end do no work (no shuffles
-    // cross row groups, and a row group is either fully valid or fully idle).
-    if (g >= total) return;
-    const int64_t b = g / n_rows;
-    const int64_t i = g - b * n_rows;
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + (b * x_seq_stride + i) * LK_DIM + sub * 16);
+struct KeyJob {
+    const uint16_t *x;
+    int64_t n_seq, n_rows, x_seq_stride;
+    uint8_t *cache;
+    float *cache_scale;
+    int64_t cache_seq_stride, cache_rows, row_offset;
+    const int32_t *positions;
+};
+
+struct QueryJob {
+    const uint16_t *q;
+    const float *w;
+    int64_t n_rows;
+    uint8_t *q_fp8;
+    float *w_eff, *q_scale;
+};
+
+// Row g of the key job, owned by the 8 lanes of this row group (sub = lane in group).
+__device__ __forceinline__ void key_row(const KeyJob &k, int64_t g, int sub) {
+    const int64_t b = g / k.n_rows;
+    const int64_t i = g - b * k.n_rows;
+    const uint4 *src = reinterpret_cast<const uint4 *>(k.x + (b * k.x_seq_stride + i) * LK_DIM + sub * 16);
     uint4 v0 = src[0], v1 = src[1];
     uint32_t in[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint32_t out[4];
     int j;
     quantize_row16(in, out, j);
-    const int64_t p = (positions ? (int64_t)positions[b] : row_offset) + i;
-    if (p < 0 || p >= cache_rows) return;
-    const int64_t row = b * cache_seq_stride + p;
-    *reinterpret_cast<uint4 *>(cache + row * LK_DIM + sub * 16) = make_uint4(out[0], out[1], out[2], out[3]);
-    if (sub == 0) cache_scale[row] = __builtin_ldexpf(1.0f, j);
+    const int64_t p = (k.positions ? (int64_t)k.positions[b] : k.row_offset) + i;
+    if (p < 0 || p >= k.cache_rows) return;
+    const int64_t row = b * k.cache_seq_stride + p;
+    *reinterpret_cast<uint4 *>(k.cache + row * LK_DIM + sub * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+    if (sub == 0) k.cache_scale[row] = __builtin_ldexpf(1.0f, j);
 }
 
-__global__ void __launch_bounds__(256)
-quantize_queries_kernel(const uint16_t *__restrict__ q, const float *__restrict__ w, int64_t n_rows,
-                        uint8_t *__restrict__ q_fp8, float *__restrict__ w_eff,
-                        float *__restrict__ q_scale) {
-    const int64_t g = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 3);
-    const int sub = threadIdx.x & 7;
-    if (g >= n_rows) return;
-    const uint4 *src = reinterpret_cast<const uint4 *>(q + g * LK_DIM + sub * 16);
+__device__ __forceinline__ void query_row(const QueryJob &q, int64_t g, int sub) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(q.q + g * LK_DIM + sub * 16);
     uint4 v0 = src[0], v1 = src[1];
     uint32_t in[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint32_t out[4];
     int j;
     quantize_row16(in, out, j);
-    *reinterpret_cast<uint4 *>(q_fp8 + g * LK_DIM + sub * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+    *reinterpret_cast<uint4 *>(q.q_fp8 + g * LK_DIM + sub * 16) = make_uint4(out[0], out[1], out[2], out[3]);
     if (sub == 0) {
         const float s = __builtin_ldexpf(1.0f, j);
-        const float ws = __fmul_rn(w[g], s);          // exact unless it leaves the float range
-        w_eff[g] = __fmul_rn(ws, kSoftmaxScale);
-        if (q_scale) q_scale[g] = s;
+        const float ws = __fmul_rn(q.w[g], s);        // exact unless it leaves the float range
+        q.w_eff[g] = __fmul_rn(ws, kSoftmaxScale);
+        if (q.q_scale) q.q_scale[g] = s;
+    }
+}
+
+// Blocks [0, key_blocks) write keys, the rest quantize queries.  A row group past its
+// job's end does no work (no shuffle crosses row groups, so a group is either fully
+// valid or fully idle).
+__global__ void __launch_bounds__(256)
+quantize_kernel(KeyJob kj, QueryJob qj, int64_t key_blocks) {
+    const int sub = threadIdx.x & 7;
+    if ((int64_t)blockIdx.x < key_blocks) {
+        const int64_t g = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 3);
+        if (g < kj.n_seq * kj.n_rows) key_row(kj, g, sub);
+    } else {
+        const int64_t g = ((int64_t)blockIdx.x - key_blocks) * kRowsPerBlock + (threadIdx.x >> 3);
+        if (g < qj.n_rows) query_row(qj, g, sub);
     }
 }
 
 }  // namespace
 
-hipError_t launch_quantize_keys(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride,
-                                uint8_t *cache, float *cache_scale, int64_t cache_seq_stride,
-                                int64_t cache_rows, int64_t row_offset, const int32_t *positions,
-                                hipStream_t stream) {
-    const int64_t total = n_seq * n_rows;
-    const int64_t blocks = (total + kRowsPerBlock - 1) / kRowsPerBlock;
-    return launch(quantize_keys_kernel, dim3((unsigned)blocks), dim3(256), 0u, stream, x, n_seq, n_rows,
-                       x_seq_stride, cache, cache_scale, cache_seq_stride, cache_rows, row_offset, positions);
-}
-
-hipError_t launch_quantize_queries(const uint16_t *q, const float *w, int64_t n_rows, uint8_t *q_fp8,
-                                   float *w_eff, float *q_scale, hipStream_t stream) {
-    const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    return launch(quantize_queries_kernel, dim3((unsigned)blocks), dim3(256), 0u, stream, q, w, n_rows,
-                       q_fp8, w_eff, q_scale);
+// Either job may be empty (n rows == 0); one launch covers both.
+hipError_t launch_quantize(const KeyJobArgs &ka, const QueryJobArgs &qa, hipStream_t stream) {
+    KeyJob kj{ka.x, ka.n_seq, ka.n_rows, ka.x_seq_stride, ka.cache, ka.cache_scale, ka.cache_seq_stride,
+              ka.cache_rows, ka.row_offset, ka.positions};
+    QueryJob qj{qa.q, qa.w, qa.n_rows, qa.q_fp8, qa.w_eff, qa.q_scale};
+    const int64_t key_blocks = (ka.n_seq * ka.n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int64_t query_blocks = (qa.n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    return launch(quantize_kernel, dim3((unsigned)(key_blocks + query_blocks)), dim3(256), 0u, stream, kj, qj,
+                  key_blocks);
 }
 
 }  // namespace lk

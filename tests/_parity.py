@@ -90,7 +90,8 @@ class GpuResult:
 
 def gpu_pipeline(inp: W.Inputs, device="cuda:0", new_rows_only: bool = False) -> GpuResult:
     """The hot path through the C ABI: cache prefix written first, then one step:
-    key write of the step's rows, query quantize + fold, index score, top-k."""
+    key write of the step's rows with query quantize + fold (one lk_prepare launch),
+    index score, top-k."""
     from sparse_attention_lightning_fp8_amd import api
     wl = inp.wl
     k = inp.k.to(device)
@@ -103,11 +104,10 @@ def gpu_pipeline(inp: W.Inputs, device="cuda:0", new_rows_only: bool = False) ->
     for b in range(wl.B):
         p0 = int(inp.positions[b])
         rows_step[b] = k[b, p0:p0 + wl.S]
-    api.lk_quantize_keys(rows_step, cache, cache_scale, positions=positions)
     q = inp.q.to(device)
     w = inp.w.to(device)
     q_scale = torch.empty_like(w)
-    q_fp8, w_eff = api.lk_quantize_queries(q, w, q_scale=q_scale)
+    q_fp8, w_eff = api.lk_prepare(rows_step, cache, cache_scale, q, w, positions=positions, q_scale=q_scale)
     seq_len = inp.lens.to(device) if inp.lens is not None else None
     scores = api.lk_index_score(q_fp8, w_eff, cache, cache_scale, wl.T, start_pos=wl.start_pos,
                                 seq_len=seq_len, causal=wl.causal)

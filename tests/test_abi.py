@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     assert syms == sorted(["lk_quantize_keys", "lk_quantize_queries", "lk_index_score", "lk_topk",
-                           "lk_profile_next_launch", "lk_status_string", "lk_abi_version"])
+                           "lk_prepare", "lk_profile_next_launch", "lk_status_string", "lk_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -72,6 +72,18 @@ def test_quantize_queries_validation(lib):
     assert f(A, A, 1, 64, A + 4, A, None, None) == E_UNSUP
     assert f(A, A, 1, 64, A, A, A + 1, None) == E_UNSUP
     assert f(None, None, 0, 64, None, None, None, None) == OK
+
+
+def test_prepare_validation(lib):
+    f = lib.lk_prepare
+    K = (A, 1, 1, 1, A, A, 16, 16, 0, None)
+    Q = (A, A, 1, 64, A, A, None)
+    assert f(A, -1, 1, 1, A, A, 16, 16, 0, None, *Q, None) == E_SHAPE
+    assert f(*K, A, A, -1, 64, A, A, None, None) == E_SHAPE
+    assert f(*K, None, A, 1, 64, A, A, None, None) == E_NULL
+    assert f(None, 1, 1, 1, A, A, 16, 16, 0, None, *Q, None) == E_NULL
+    assert f(*K, A + 4, A, 1, 64, A, A, None, None) == E_UNSUP
+    assert f(None, 0, 0, 0, None, None, 0, 0, 0, None, None, None, 0, 64, None, None, None, None) == OK
 
 
 def test_index_score_validation(lib):

@@ -133,3 +133,27 @@ def test_queries_and_weight_fold_bit_exact():
     assert np.array_equal(q8.cpu().numpy().reshape(-1, 128), oc)
     assert np.array_equal(qs.cpu().numpy().reshape(-1).view(np.uint32), os_.view(np.uint32))
     assert np.array_equal(we.cpu().numpy().reshape(-1).view(np.uint32), ow.view(np.uint32))
+
+
+def test_prepare_equals_separate_calls():
+    g = torch.Generator().manual_seed(103)
+    x = torch.randn(3, 7, 128, generator=g).to(torch.bfloat16).to(DEV)
+    q = torch.randn(5, 64, 128, generator=g).to(torch.bfloat16).to(DEV)
+    w = (torch.randn(5, 64, generator=g) * 0.125).to(DEV)
+    pos = torch.tensor([0, 20, 41], dtype=torch.int32, device=DEV)
+    c1 = torch.zeros(3, 48, 128, dtype=torch.uint8, device=DEV)
+    s1 = torch.zeros(3, 48, device=DEV)
+    c2, s2 = c1.clone(), s1.clone()
+    log("[quantize] lk_prepare vs separate calls")
+    api.lk_quantize_keys(x, c1, s1, positions=pos)
+    q8a, wa = api.lk_quantize_queries(q, w)
+    q8b, wb = api.lk_prepare(x, c2, s2, q, w, positions=pos)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(q8a, q8b) and torch.equal(wa.view(torch.int32), wb.view(torch.int32))
+    # one job empty
+    c3, s3 = torch.zeros_like(c1), torch.zeros_like(s1)
+    api.lk_prepare(x[:, :0], c3, s3, q, w, positions=pos)
+    q8c, wc = api.lk_prepare(x, c3, s3, q[:0], w[:0], positions=pos)
+    torch.cuda.synchronize()
+    assert torch.equal(c3, c1) and q8c.numel() == 0
