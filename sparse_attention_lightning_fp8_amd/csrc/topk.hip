@@ -6,19 +6,33 @@
 // -0 equal to +0, unused slots -1.
 //
 // One block of 1024 threads per row.  The row is read from HBM once and stays in
-// registers: thread t holds elements 4(t + 1024 j) + c (j, c < 4) as order-preserving
-// 32-bit keys.  A radix select walks the key from the top with digits of 12, 11 and
-// 9 bits; each pass histograms (in LDS) the next digit of the elements that still
-// match the chosen prefix, and a block scan picks the bin holding the k-th largest.  As
-// soon as the chosen bin is taken whole, the remaining digits cannot change the
-// selected set and the walk stops (the common case after two passes).  The write-out
-// ranks the selected elements with one block-wide scan of packed per-thread counts, so
-// the result is deterministic: every index whose key is above the final prefix in
-// increasing order, then the lowest-index elements equal to it.
+// registers: thread t holds elements 4(t + 1024 j) + c (j, c < 4).
 //
-// The histogram has four copies (lane & 3 picks one; copies are padded onto different
-// banks) so that lanes of one wave that hit the same bin mostly update different
-// words.  Wave-level scans use DPP row shifts and row broadcasts.
+// 1. A block reduction finds the row's smallest and largest valid score, lo and hi.
+// 2. Each element goes to one of 4096 equal-width bins of [lo, hi]:
+//    bin(v) = min(4095, trunc((v - lo) * (4096 / (hi - lo)))).  Rounded subtraction
+//    and multiplication by a positive constant are monotone, so v1 < v2 implies
+//    bin(v1) <= bin(v2): every element of a higher bin outranks every element of a
+//    lower one.  Unlike digits of the float's bits, equal-width bins spread the
+//    scores of a row evenly, so LDS histogram updates rarely collide and the bin
+//    that holds the k-th largest score holds few elements.
+// 3. A block scan of the histogram from the top finds that bin b and how many of
+//    its elements are still needed.
+// 4. Inside bin b the exact cut is found: if the bin is taken whole, nothing more;
+//    if it holds at most 64 elements, one wave ranks them pairwise (score
+//    descending, index ascending); otherwise a radix select walks the 32-bit
+//    order-preserving key of the bin's elements with digits of 12, 11 and 9 bits.
+//    A row whose range is empty or outside [1e-30, 1e30] puts every element in
+//    bin 0 and takes the radix path.
+// 5. The write-out ranks the selected elements with one block-wide scan of packed
+//    per-thread counts, so the result is deterministic: an upper group (the higher
+//    bins and the part of the cut bin above the cut) in increasing index order, then
+//    the cut group (the taken elements at the cut, lowest indices first) in
+//    increasing index order.  Every score of the upper group exceeds every score of
+//    the cut group; the cut group is one value except when a bin or digit is taken
+//    whole.
+//
+// Wave-level scans and reductions use DPP row shifts and row broadcasts.
 #include "lk_device.h"
 
 namespace lk {
@@ -28,8 +42,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPer = 16;                    // elements per thread (kThreads * kPer == LK_TOPK_MAX_T)
 constexpr int kBins = 4096;
-constexpr int kCopies = 4;
-constexpr int kCopyStride = kBins + 4;      // +4 words: copies start on different banks, 16-B aligned
+constexpr int kSmall = 64;                  // a cut bin this small is ranked pairwise by one wave
 
 // Larger float -> larger key; -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float v) {
@@ -49,27 +62,57 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
     return x;
 }
 
+// Running maximum and minimum over the lanes of a wave, ignoring NaN lanes (lanes
+// that DPP cannot source read NaN, which fmaxf/fminf ignore); lane 63 ends with the
+// wave's result.
+#define LK_DPP_F(x, ctrl, rm) __int_as_float(__builtin_amdgcn_update_dpp(0x7FC00000, __float_as_int(x), ctrl, rm, 0xf, false))
+__device__ __forceinline__ float wave_fmax(float x) {
+    x = fmaxf(x, LK_DPP_F(x, 0x111, 0xf));
+    x = fmaxf(x, LK_DPP_F(x, 0x112, 0xf));
+    x = fmaxf(x, LK_DPP_F(x, 0x114, 0xf));
+    x = fmaxf(x, LK_DPP_F(x, 0x118, 0xf));
+    x = fmaxf(x, LK_DPP_F(x, 0x142, 0xa));
+    x = fmaxf(x, LK_DPP_F(x, 0x143, 0xc));
+    return x;
+}
+__device__ __forceinline__ float wave_fmin(float x) {
+    x = fminf(x, LK_DPP_F(x, 0x111, 0xf));
+    x = fminf(x, LK_DPP_F(x, 0x112, 0xf));
+    x = fminf(x, LK_DPP_F(x, 0x114, 0xf));
+    x = fminf(x, LK_DPP_F(x, 0x118, 0xf));
+    x = fminf(x, LK_DPP_F(x, 0x142, 0xa));
+    x = fminf(x, LK_DPP_F(x, 0x143, 0xc));
+    return x;
+}
+#undef LK_DPP_F
+
+// Sum of the per-wave totals of waves 0 .. wave-1 (before) and of all kWaves waves
+// (total), computed by every wave from the kWaves words of `part` (one per wave).
+__device__ __forceinline__ void wave_prefix(const uint32_t *part, int wave, uint32_t &before, uint32_t &total) {
+    const int lane = __lane_id();
+    const uint32_t s = wave_scan(lane < kWaves ? part[lane] : 0u);
+    total = (uint32_t)__builtin_amdgcn_readlane((int)s, kWaves - 1);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)s, (wave + kWaves - 1) & (kWaves - 1));
+    before = wave > 0 ? b : 0u;
+}
+
 // Block-wide selection: the bin holding the need-th largest counted element (counting
 // from the top bin) and the number of counted elements in higher bins; writes
-// (bin, above, count) to sel.  Thread t owns bins 4095-4t .. 4092-4t (one 16-byte read
-// per histogram copy, conflict-free), scans within its wave with DPP and across waves
-// through wsum.  Ends with a barrier after which sel is valid.
+// (bin, above, count) to sel.  Thread t owns bins 4095-4t .. 4092-4t (one 16-byte
+// read), scans within its wave with DPP and across waves through wsum.  Ends with a
+// barrier after which sel is valid.
 __device__ __forceinline__ void select_bin(const uint32_t *hist, uint32_t need, uint32_t *wsum, uint32_t *sel) {
     const int tid = threadIdx.x, lane = __lane_id(), wave = tid >> 6;
     const int lo = kBins - 4 - 4 * tid;                // bins lo .. lo+3, owned top-down
-    uint32_t c[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int cp = 0; cp < kCopies; cp++) {
-        const uint32_t *h = hist + cp * kCopyStride + lo;
-#pragma unroll
-        for (int q = 0; q < 4; q++) c[q] += h[3 - q];  // c[q] = bin lo+3-q
-    }
-    const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+    const uint4 h = *reinterpret_cast<const uint4 *>(hist + lo);
+    const uint32_t mine = h.x + h.y + h.z + h.w;
     const uint32_t incl = wave_scan(mine);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    uint32_t above = incl - mine;
-    for (int w = 0; w < wave; w++) above += wsum[w];
+    uint32_t before, total;
+    wave_prefix(wsum, wave, before, total);
+    uint32_t above = before + incl - mine;
+    const uint32_t c[4] = {h.w, h.z, h.y, h.x};        // c[q] = bin lo+3-q
 #pragma unroll
     for (int q = 0; q < 4; q++) {
         if (above < need && above + c[q] >= need) {
@@ -82,12 +125,25 @@ __device__ __forceinline__ void select_bin(const uint32_t *hist, uint32_t need, 
     __syncthreads();
 }
 
-__global__ void __launch_bounds__(kThreads)
+__device__ __forceinline__ void clear_hist(uint32_t *hist) {
+    reinterpret_cast<uint4 *>(hist)[threadIdx.x] = make_uint4(0, 0, 0, 0);   // kThreads * 4 == kBins
+}
+
+// Index of element e of thread tid.
+__device__ __forceinline__ uint32_t elem_index(int tid, int e) {
+    return 4u * tid + 4u * kThreads * (e >> 2) + (e & 3);
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *__restrict__ idx) {
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kCopies * kCopyStride + 3];
-    __shared__ uint32_t wtot[kWaves][4];
+    static_assert(kThreads * 4 == kBins && kThreads * kPer == LK_TOPK_MAX_T && kWaves == 16, "tiling");
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kBins + 4];   // + a spare word for invalid elements
+    __shared__ uint32_t wtot[4][kWaves];
     __shared__ uint32_t wsum[kWaves];
+    __shared__ float wred[2][kWaves];
     __shared__ uint32_t sel[3];
+    __shared__ uint32_t cand_key[kSmall], cand_idx[kSmall];
+    __shared__ uint32_t ccount, cut[2];
 
     const int row = blockIdx.x;
     const int b = row / rows.S;
@@ -103,127 +159,187 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
     const int n = (int)L;                              // k < L <= T <= LK_TOPK_MAX_T
     const float *src = scores + (int64_t)row * T;
 
-    for (int i = tid; i < kCopies * kCopyStride; i += kThreads) hist[i] = 0;
-    // Element (j, c) of this thread is index 4 (tid + 1024 j) + c.
-    uint32_t key[kPer];
-    uint32_t valid = 0;                                // bit 4j + c
-    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+    clear_hist(hist);
+    if (tid == 0) ccount = 0;
+    // Element e of this thread has index elem_index(tid, e); elements past the valid
+    // prefix hold NaN.  Group j (elements 4j..4j+3) of a wave is `live` when it holds
+    // at least one valid element; a dead group is skipped by every later pass.
+    const float qnan = __int_as_float(0x7FC00000);
+    float v[kPer];
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (T & 3) == 0;
+    const int rem = n - 4 * tid;                       // element e is valid iff its offset < rem
+    const int wave_rem = n - 4 * 64 * wave;            // the same for the wave's first lane
+    auto live = [&](int j) { return 4 * kThreads * j < wave_rem; };
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const int i0 = 4 * (tid + kThreads * j);
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        if (vec && i0 + 3 < n) {
-            const float4 x = *reinterpret_cast<const float4 *>(src + i0);
-            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; c++)
-                if (i0 + c < n) v[c] = src[i0 + c];
+        const int o = 4 * kThreads * j;
+        float4 x = make_float4(qnan, qnan, qnan, qnan);
+        if (live(j)) {
+            if (vec) {
+                // A float4 group that starts below n ends below T (T % 4 == 0): in bounds.
+                if (o < rem) x = *reinterpret_cast<const float4 *>(src + 4 * tid + o);
+                if (o + 1 >= rem) x.y = qnan;
+                if (o + 2 >= rem) x.z = qnan;
+                if (o + 3 >= rem) x.w = qnan;
+            } else {
+                if (o < rem) x.x = src[4 * tid + o];
+                if (o + 1 < rem) x.y = src[4 * tid + o + 1];
+                if (o + 2 < rem) x.z = src[4 * tid + o + 2];
+                if (o + 3 < rem) x.w = src[4 * tid + o + 3];
+            }
         }
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            key[4 * j + c] = order_key(v[c]);
-            if (i0 + c < n) valid |= 1u << (4 * j + c);
-        }
+        v[4 * j] = x.x; v[4 * j + 1] = x.y; v[4 * j + 2] = x.z; v[4 * j + 3] = x.w;
     }
-    uint32_t *my_hist = hist + (lane & (kCopies - 1)) * kCopyStride;
-    __syncthreads();
 
-    // Radix select from the top: digits of 12, 11 and 9 bits.
-    uint32_t prefix = 0, pmask = 0, need = (uint32_t)k;
-    const int shifts[3] = {20, 9, 0};
-    const uint32_t dmasks[3] = {0xFFFu, 0x7FFu, 0x1FFu};
-#pragma unroll 1
-    for (int pass = 0; pass < 3; pass++) {
-        const int sh = shifts[pass];
-        const uint32_t dm = dmasks[pass];
+    // 1. Row range (NaN entries are ignored by fmaxf / fminf).
+    float mx = v[0], mn = v[0];
 #pragma unroll
-        for (int e = 0; e < kPer; e++)
-            if (((valid >> e) & 1u) && (key[e] & pmask) == prefix) atomicAdd(&my_hist[(key[e] >> sh) & dm], 1u);
-        __syncthreads();
-        select_bin(hist, need, wsum, sel);
-        const uint32_t d = sel[0], ab = sel[1], cnt = sel[2];
-        need -= ab;
-        prefix |= d << sh;
-        pmask |= dm << sh;
-        if (need == cnt || pass == 2) break;           // the whole bin is taken (or K* is exact)
-        for (int i = tid; i < kCopies * kCopyStride; i += kThreads) hist[i] = 0;
-        __syncthreads();
+    for (int e = 1; e < kPer; e++) {
+        mx = fmaxf(mx, v[e]);
+        mn = fminf(mn, v[e]);
     }
-    // Selected: (key & pmask) > prefix  (n_gt of them), and the `need` lowest-index
-    // elements with (key & pmask) == prefix.
-    const uint32_t n_gt = (uint32_t)k - need;
+    mx = wave_fmax(mx);
+    mn = wave_fmin(mn);
+    if (lane == 63) {
+        wred[0][wave] = mx;
+        wred[1][wave] = mn;
+    }
+    __syncthreads();
+    // Every wave reduces the kWaves partial results itself (lane l reads wave l % 16).
+    mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_fmax(wred[0][lane & (kWaves - 1)])), 63));
+    mn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_fmin(wred[1][lane & (kWaves - 1)])), 63));
+    const float width = mx - mn;
+    const bool spread = width >= 1e-30f && width <= 1e30f;
+    // scale = 4095 / width keeps (mx - mn) * scale below 4096 despite rounding, and
+    // every valid score of a spread row is finite, so bins are 0 .. 4095.
+    const float lo = spread ? mn : 0.f, scale = spread ? 4095.f / width : 0.f;
+    auto bin_of = [&](float x) -> uint32_t { return spread ? (uint32_t)((x - lo) * scale) : 0u; };
+
+    // 2-3. Histogram of the bins, then the bin holding the k-th largest.
+#pragma unroll
+    for (int e = 0; e < kPer; e++) {
+        if (!live(e >> 2)) continue;
+        const bool ok = v[e] == v[e];                  // invalid elements count in the spare word
+        atomicAdd(&hist[ok ? bin_of(v[e]) : (uint32_t)kBins], 1u);
+    }
+    __syncthreads();
+    select_bin(hist, (uint32_t)k, wsum, sel);
+    const uint32_t cb = sel[0], cnt = sel[2];
+    uint32_t need = (uint32_t)k - sel[1];
+
+    // 4. Classify: gbits = elements of higher bins (taken), ebits = elements of bin cb.
     uint32_t gbits = 0, ebits = 0;
 #pragma unroll
     for (int e = 0; e < kPer; e++) {
-        const uint32_t m = key[e] & pmask;
-        if ((valid >> e) & 1u) {
-            gbits |= (m > prefix ? 1u : 0u) << e;
-            ebits |= (m == prefix ? 1u : 0u) << e;
+        if (!live(e >> 2)) continue;
+        const uint32_t bn = bin_of(v[e]);
+        const bool ok = v[e] == v[e];
+        gbits |= (ok && bn > cb ? 1u : 0u) << e;
+        ebits |= (ok && bn == cb ? 1u : 0u) << e;
+    }
+    // The cut inside bin cb: of its elements, those whose key & pmask exceeds prefix
+    // join gbits, and the `need` lowest-index ones whose key & pmask equals prefix
+    // stay in ebits.  A bin taken whole needs no cut.
+    uint32_t prefix = 0, pmask = 0;
+    if (need < cnt && cnt <= kSmall) {
+        for (uint32_t m = ebits; m; m &= m - 1) {
+            const int e = __builtin_ctz(m);
+            const uint32_t slot = atomicAdd(&ccount, 1u);
+            cand_key[slot] = order_key(v[e]);
+            cand_idx[slot] = elem_index(tid, e);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const uint32_t mk = lane < (int)cnt ? cand_key[lane] : 0u, mi = lane < (int)cnt ? cand_idx[lane] : 0u;
+            uint32_t gt = 0, eq_before = 0;
+            for (uint32_t j = 0; j < cnt; j++) {
+                const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)j);
+                const uint32_t ij = (uint32_t)__builtin_amdgcn_readlane((int)mi, (int)j);
+                gt += kj > mk ? 1u : 0u;
+                eq_before += (kj == mk && ij < mi) ? 1u : 0u;
+            }
+            if (lane < (int)cnt && gt + eq_before == need - 1) {   // the need-th candidate: the cut
+                cut[0] = mk;
+                cut[1] = need - gt;
+            }
+        }
+        __syncthreads();
+        prefix = cut[0];
+        pmask = 0xFFFFFFFFu;
+        need = cut[1];
+    } else if (need < cnt) {
+#pragma unroll 1
+        for (int pass = 0; pass < 3; pass++) {       // digits: key bits 31-20, 19-9, 8-0
+            clear_hist(hist);
+            __syncthreads();
+            const int sh = pass == 0 ? 20 : pass == 1 ? 9 : 0;
+            const uint32_t dm = pass == 0 ? 0xFFFu : pass == 1 ? 0x7FFu : 0x1FFu;
+            for (uint32_t m = ebits; m; m &= m - 1) {
+                const uint32_t kk = order_key(v[__builtin_ctz(m)]);
+                if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> sh) & dm], 1u);
+            }
+            __syncthreads();
+            select_bin(hist, need, wsum, sel);
+            const uint32_t d = sel[0], ab = sel[1], dcnt = sel[2];
+            need -= ab;
+            prefix |= d << sh;
+            pmask |= dm << sh;
+            if (need == dcnt) break;                   // the whole digit bin is taken (or the key is exact)
         }
     }
-    // Per-row-j counts in 16-bit fields: g01 = rows 0,1 of gbits; g23 = rows 2,3; same for e.
+    if (pmask) {
+        for (uint32_t m = ebits; m; m &= m - 1) {
+            const int e = __builtin_ctz(m);
+            const uint32_t km = order_key(v[e]) & pmask;
+            if (km != prefix) ebits &= ~(1u << e);
+            if (km > prefix) gbits |= 1u << e;
+        }
+    }
+
+    // 5. Write-out.
+    const uint32_t n_gt = (uint32_t)k - need;
+    // Per-row-j counts in 16-bit fields: word 0 = rows 0,1 of gbits; 1 = rows 2,3;
+    // words 2, 3 the same for ebits.
     uint32_t cnt4[4];
-    {
-        const uint32_t g0 = __builtin_popcount(gbits & 0xFu), g1 = __builtin_popcount((gbits >> 4) & 0xFu);
-        const uint32_t g2 = __builtin_popcount((gbits >> 8) & 0xFu), g3 = __builtin_popcount((gbits >> 12) & 0xFu);
-        const uint32_t e0 = __builtin_popcount(ebits & 0xFu), e1 = __builtin_popcount((ebits >> 4) & 0xFu);
-        const uint32_t e2 = __builtin_popcount((ebits >> 8) & 0xFu), e3 = __builtin_popcount((ebits >> 12) & 0xFu);
-        cnt4[0] = g0 | (g1 << 16);
-        cnt4[1] = g2 | (g3 << 16);
-        cnt4[2] = e0 | (e1 << 16);
-        cnt4[3] = e2 | (e3 << 16);
+#pragma unroll
+    for (int f = 0; f < 4; f++) {
+        const uint32_t bits = (f < 2 ? gbits : ebits) >> (8 * (f & 1));
+        cnt4[f] = __builtin_popcount(bits & 0xFu) | (__builtin_popcount((bits >> 4) & 0xFu) << 16);
     }
     uint32_t incl[4];
 #pragma unroll
-    for (int f = 0; f < 4; f++) incl[f] = wave_scan(cnt4[f]);
-    if (lane == 63) {
-#pragma unroll
-        for (int f = 0; f < 4; f++) wtot[wave][f] = incl[f];
+    for (int f = 0; f < 4; f++) {
+        incl[f] = wave_scan(cnt4[f]);
+        if (lane == 63) wtot[f][wave] = incl[f];
     }
     __syncthreads();
-    uint32_t before[4] = {0, 0, 0, 0}, total[4] = {0, 0, 0, 0};
-    for (int w = 0; w < kWaves; w++) {
-#pragma unroll
-        for (int f = 0; f < 4; f++) {
-            const uint32_t x = wtot[w][f];
-            before[f] += w < wave ? x : 0u;
-            total[f] += x;
-        }
-    }
-    // Exclusive prefix per row j for "greater" (fields of words 0,1) and "equal" (2,3).
-    uint32_t gpre[4], epre[4], gtot[4], etot[4];
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const uint32_t gx = incl[h] - cnt4[h] + before[h], ex = incl[2 + h] - cnt4[2 + h] + before[2 + h];
-        gpre[2 * h] = gx & 0xFFFFu;
-        gpre[2 * h + 1] = gx >> 16;
-        epre[2 * h] = ex & 0xFFFFu;
-        epre[2 * h + 1] = ex >> 16;
-        gtot[2 * h] = total[h] & 0xFFFFu;
-        gtot[2 * h + 1] = total[h] >> 16;
-        etot[2 * h] = total[2 + h] & 0xFFFFu;
-        etot[2 * h + 1] = total[2 + h] >> 16;
-    }
     uint32_t gbase = 0, ebase = 0;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        uint32_t gm = (gbits >> (4 * j)) & 0xFu, em = (ebits >> (4 * j)) & 0xFu;
-        uint32_t gr = gbase + gpre[j], er = ebase + epre[j];
-        while (gm) {
-            const int c = __builtin_ctz(gm);
-            gm &= gm - 1;
-            if (gr < n_gt) out[gr] = 4 * (tid + kThreads * j) + c;
-            gr++;
+    for (int h = 0; h < 2; h++) {
+        uint32_t gb, gt, eb, et;
+        wave_prefix(wtot[h], wave, gb, gt);
+        wave_prefix(wtot[2 + h], wave, eb, et);
+        const uint32_t gx = incl[h] - cnt4[h] + gb, ex = incl[2 + h] - cnt4[2 + h] + eb;
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            const int j = 2 * h + half;
+            uint32_t gm = (gbits >> (4 * j)) & 0xFu, em = (ebits >> (4 * j)) & 0xFu;
+            uint32_t gr = gbase + ((gx >> (16 * half)) & 0xFFFFu), er = ebase + ((ex >> (16 * half)) & 0xFFFFu);
+            while (gm) {
+                const int c = __builtin_ctz(gm);
+                gm &= gm - 1;
+                if (gr < n_gt) out[gr] = 4 * (tid + kThreads * j) + c;
+                gr++;
+            }
+            while (em) {
+                const int c = __builtin_ctz(em);
+                em &= em - 1;
+                if (er < need) out[n_gt + er] = 4 * (tid + kThreads * j) + c;
+                er++;
+            }
+            gbase += (gt >> (16 * half)) & 0xFFFFu;
+            ebase += (et >> (16 * half)) & 0xFFFFu;
         }
-        while (em) {
-            const int c = __builtin_ctz(em);
-            em &= em - 1;
-            if (er < need) out[n_gt + er] = 4 * (tid + kThreads * j) + c;
-            er++;
-        }
-        gbase += gtot[j];
-        ebase += etot[j];
     }
 }
 
