@@ -5,8 +5,11 @@ tokens, query rotate/quantize + weight fold, fp8 index score with mask, per-row 
 The step rate comes from an uninstrumented timed loop; per-kernel durations come from a
 second pass of the same steps with events recorded at each dispatch's start and end.
 The timed workload is decode with 16 sequences of 16384 cached keys (64 heads x 128,
-top-2048); every input is resident in HBM before timing, and R copies of the inputs
-are rotated so the 256 MB last-level cache cannot serve the 33 MB key cache.
+top-2048), run as lk_decode_score (key write + query preparation + score in one
+launch) then lk_topk; every input is resident in HBM before timing, and R copies of
+the inputs are rotated so the 256 MB last-level cache cannot serve the 33 MB key
+cache.  The same step through the separate entry points (lk_prepare, lk_index_score,
+lk_topk) is timed too and reported under "extra".
 
 Prints ONE JSON line.  Prefill (4096x4096 causal) and chunked prefill (2 x 4096 new
 tokens against 16384 keys) are timed too and reported under "extra".
@@ -32,7 +35,8 @@ BYTES_PER_KEY = 136           # 128 B key + 4 B key scale + 4 B score
 BYTES_PER_QUERY_ROW = 64 * (128 + 4)
 FLOP_PER_PAIR = 2 * 64 * 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-SCORE_SRC = os.path.join(ROOT, "sparse_attention_lightning_fp8_amd", "csrc", "score.hip")
+SCORE_SRCS = [os.path.join(ROOT, "sparse_attention_lightning_fp8_amd", "csrc", f)
+              for f in ("score.hip", "quant_device.h", "lk_device.h")]
 
 
 def log(msg):
@@ -111,6 +115,24 @@ def raw_calls(wl, s):
     ]
 
 
+def raw_calls_fused(wl, s):
+    """The same step as raw_calls through lk_decode_score + lk_topk (decode rows only)."""
+    import ctypes
+    import torch
+    from sparse_attention_lightning_fp8_amd import _lib
+    lib = _lib.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    cap = s.cache.shape[1]
+    seq_len = s.seq_len.data_ptr() if s.seq_len is not None else None
+    s.rows = _lib.LkRows(wl.B, wl.S, wl.T, wl.start_pos, seq_len, 1 if wl.causal else 0)
+    rows = ctypes.byref(s.rows)
+    return [
+        (lib.lk_decode_score, (s.q.data_ptr(), s.w.data_ptr(), 64, s.k_new.data_ptr(), s.cache.data_ptr(),
+                               s.cache_scale.data_ptr(), cap, rows, s.scores.data_ptr(), None, None, stream)),
+        (lib.lk_topk, (s.scores.data_ptr(), rows, wl.k, s.idx.data_ptr(), stream)),
+    ]
+
+
 def run_step(calls, ev=None, arm=None):
     """One pass of the hot path (lk_prepare: key write + query quantize and weight fold;
     lk_index_score; lk_topk).  `ev` (optional) holds one (start, stop) event pair per
@@ -136,21 +158,23 @@ def make_event_pairs(n_steps, n_kernels):
     return evs
 
 
-def time_workload(api, wl_name, steps, warmup, n_sets, dev):
+def time_workload(api, wl_name, steps, warmup, n_sets, dev, fused=False):
     """Warm up, then time `steps` uninstrumented steps (wall clock between two device
     synchronizations: this gives the step rate), then run the same `steps` again with
-    dispatch events armed on every kernel (this gives each kernel's mean duration)."""
+    dispatch events armed on every kernel (this gives each kernel's mean duration).
+    `fused` runs the decode step as lk_decode_score + lk_topk."""
     import torch
     from sparse_attention_lightning_fp8_amd import _lib
     from sparse_attention_lightning_fp8_amd import workloads as W
     wl = W.WORKLOADS[wl_name]
     inp = W.make_inputs(wl, seed=0)
     sets = make_sets(api, inp, n_sets, dev)
-    calls = [raw_calls(wl, s) for s in sets]
+    calls = [(raw_calls_fused if fused else raw_calls)(wl, s) for s in sets]
     arm = _lib.load().lk_profile_next_launch
     for i in range(warmup):
         run_step(calls[i % n_sets])
-    evs = make_event_pairs(steps, 3)
+    names = ["decode_score", "topk"] if fused else ["prepare", "index_score", "topk"]
+    evs = make_event_pairs(steps, len(names))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -160,9 +184,22 @@ def time_workload(api, wl_name, steps, warmup, n_sets, dev):
     for i in range(steps):
         run_step(calls[i % n_sets], evs[i], arm)
     torch.cuda.synchronize()
-    names = ["prepare", "index_score", "topk"]
     per = {n: sum(e[j][0].elapsed_time(e[j][1]) for e in evs) / steps * 1e3 for j, n in enumerate(names)}
     return wl, inp, wall, per
+
+
+def fused_decode_bytes(wl, inp):
+    """Bytes lk_decode_score must move for one step: per row, the cached keys [0, L-1)
+    with their scales (132 B each), the new key (256 B of bf16 read, 132 B written),
+    every score slot (4 B), and the bf16 query with its weights (64 x 256 B + 64 x 4 B)."""
+    tot = 0
+    for b in range(wl.B):
+        L = min(wl.T, int(inp.lens[b])) if inp.lens is not None else wl.T
+        if wl.causal:
+            L = min(L, wl.start_pos + 1)
+        L = max(L, 0)
+        tot += max(L - 1, 0) * 132 + (256 + 132 if L >= 1 else 0) + wl.T * 4 + 64 * 128 * 2 + 64 * 4
+    return tot
 
 
 def valid_pairs(wl, inp):
@@ -211,12 +248,20 @@ def cpu_baseline(wl_name):
 
 
 # ---------------------------------------------------------------------------- traffic
+def source_hash():
+    """sha256 over the sources the decode score kernel is built from."""
+    h = hashlib.sha256()
+    for f in SCORE_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per score launch from committed rocprofv3 PMC runs, if they were taken
-    on the current score kernel source."""
+    on the current score kernel sources."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        h = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
+        h = source_hash()
         if rec.get("score_src_sha256") == h:
             return rec["bytes_per_launch"]
     except (OSError, ValueError, KeyError):
@@ -256,17 +301,25 @@ def main():
     torch.cuda.init()
 
     log("decode_b16_t16384: setting up")
-    wl, inp, wall, per = time_workload(api, "decode_b16_t16384", args.steps, args.warmup, args.rotate, dev)
+    _, _, uwall, uper = time_workload(api, "decode_b16_t16384", args.steps, args.warmup, args.rotate, dev)
+    torch.cuda.empty_cache()
+    wl, inp, wall, per = time_workload(api, "decode_b16_t16384", args.steps, args.warmup, args.rotate, dev,
+                                       fused=True)
     keys = wl.B * wl.S * wl.T
     ms_step = wall / args.steps * 1e3
     value = keys * args.steps / wall
-    score_bytes = keys * BYTES_PER_KEY + wl.B * wl.S * BYTES_PER_QUERY_ROW
-    score_us = per["index_score"]
+    score_bytes = fused_decode_bytes(wl, inp)
+    score_us = per["decode_score"]
     achieved = score_bytes / (score_us * 1e-6) / 1e9
-    log(f"decode: {ms_step * 1e3:.1f} us/step, kernels {per}")
+    log(f"decode (fused): {ms_step * 1e3:.1f} us/step, kernels {per}")
+    u_bytes = keys * BYTES_PER_KEY + wl.B * wl.S * BYTES_PER_QUERY_ROW
+    log(f"decode (separate calls): {uwall / args.steps * 1e6:.1f} us/step, kernels {uper}")
 
     extra = {"score_kernel_us": score_us, "score_hbm_GBps": achieved,
-             "step_kernel_us": per, "keys_per_s_score_kernel": keys / (score_us * 1e-6)}
+             "step_kernel_us": per, "keys_per_s_score_kernel": keys / (score_us * 1e-6),
+             "separate_calls": {"step_us": uwall / args.steps * 1e6, "kernel_us": uper,
+                                "index_score_hbm_GBps": u_bytes / (uper["index_score"] * 1e-6) / 1e9,
+                                "index_score_algorithmic_bytes": u_bytes}}
     if not args.no_prefill:
         for name in ("prefill_s4096", "chunked_prefill_b2_s4096"):
             log(f"{name}: setting up")
@@ -296,7 +349,7 @@ def main():
                    "topk": wl.k, "rotated_input_copies": args.rotate},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
-                     "kernel": "score_decode_kernel", "algorithmic_bytes": score_bytes},
+                     "kernel": "decode_kernel<true> (lk_decode_score)", "algorithmic_bytes": score_bytes},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -150,14 +150,39 @@ LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_
                                 float *scores, hipStream_t stream);
 
 /*
+ * One decode step of Indexer.forward up to the scores, in ONE kernel launch: the
+ * new token's key write (the cache update at [start_pos, end_pos) of the forward
+ * excerpt), the query quantization with the weight fold, and fp8_index + mask.
+ * Rows have S == 1.  For sequence b with valid length L = row length of lk_rows
+ * (L >= 1), the new key k_new[b] goes to cache slot L-1 -- the decode token's own
+ * position -- exactly as lk_quantize_keys would write it, and the scores of keys
+ * [0, L) include it.  A row with L == 0 writes nothing to the cache and scores -inf.
+ *   q      [B, heads, 128] bf16 bits;   w [B, heads] float32 (raw, 1/sqrt(64) included)
+ *   k_new  [B, 128] bf16 bits
+ *   k_cache / k_scale as in lk_index_score (written at slot L-1 of each sequence)
+ *   scores [B, 1, T] float32, identical to lk_prepare + lk_index_score on the same inputs.
+ *   q_fp8_out [B, heads, 128], w_eff_out [B, heads]: optional (both NULL or both set)
+ *   copies of the quantized query and folded weights.
+ * Every block of the kernel quantizes its row's query while its key loads are in
+ * flight, so the query preparation costs no separate launch.
+ * Requires S == 1, heads == 64, T <= cache_seq_stride; q, k_new, k_cache and
+ * q_fp8_out 16-byte aligned, w and w_eff_out 4-byte aligned.
+ */
+LK_API lk_status lk_decode_score(const uint16_t *q, const float *w, int32_t heads, const uint16_t *k_new,
+                                 uint8_t *k_cache, float *k_scale, int64_t cache_seq_stride,
+                                 const lk_rows *rows, float *scores, uint8_t *q_fp8_out,
+                                 float *w_eff_out, hipStream_t stream);
+
+/*
  * Per-row top-k of Indexer.forward (index_score.topk), with the NKI indexer's
  * int32 unordered-set result (page "DeepSeek-V3.2 Sparse Indexer Kernel API
  * Reference", Notes).  For row r = b*S + t with valid length L (see lk_rows):
  * idx[r*k + j] for j < min(k, L) holds the indices of the min(k, L) largest
  * scores among scores[r*T + 0 .. r*T + L-1]; ties go to the lower index and
- * -0 equals +0.  Slots j >= min(k, L) hold -1.  The set is written as: all
- * indices with a score strictly above the k-th largest, in increasing index
- * order, then the tied ones, in increasing index order.
+ * -0 equals +0.  Slots j >= min(k, L) hold -1.  The set is written as two runs,
+ * each in increasing index order: an upper group, then a cut group; every score
+ * of the upper group is above every score of the cut group, and within the cut
+ * group's lowest score the lower indices are the ones taken.
  * Requires k >= 1 and T <= LK_TOPK_MAX_T (else LK_E_UNSUPPORTED).
  */
 LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, int32_t *idx,

@@ -141,6 +141,46 @@ def lk_index_score(q_fp8: torch.Tensor, w_eff: torch.Tensor, k_cache: torch.Tens
     return scores
 
 
+def lk_decode_score(q: torch.Tensor, w: torch.Tensor, k_new: torch.Tensor, k_cache: torch.Tensor,
+                    k_scale: torch.Tensor, T: int, start_pos: int = 0, seq_len: Optional[torch.Tensor] = None,
+                    causal: bool = False, scores: Optional[torch.Tensor] = None,
+                    q_fp8_out: Optional[torch.Tensor] = None, w_eff_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step up to the scores in one launch: writes k_new [B, 128] (bf16) to
+    slot L-1 of each sequence's cache, quantizes q [B, 64, 128] (bf16) with weights
+    w [B, 64] (float32), and returns masked scores [B, 1, T] (float32).  Optional
+    q_fp8_out [B, 64, 128] and w_eff_out [B, 64] receive the quantized query."""
+    _need(q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[-1] == DIM, "q must be contiguous bf16 [B, H, 128]")
+    H = q.shape[-2]
+    B = q.numel() // (H * DIM) if H > 0 else 0
+    _need(w.dtype == torch.float32 and w.is_contiguous() and w.numel() == B * H, "w must be contiguous float32 [B, H]")
+    _need(k_new.dtype == torch.bfloat16 and k_new.is_contiguous() and k_new.numel() == B * DIM,
+          "k_new must be contiguous bf16 [B, 128]")
+    kc = _byte_view(k_cache)
+    _need(kc.dtype == torch.uint8 and kc.dim() == 3 and kc.shape[2] == DIM and kc.stride(2) == 1
+          and kc.stride(1) == DIM and kc.stride(0) % DIM == 0 and kc.shape[0] >= B, "bad k_cache")
+    ks = k_scale.squeeze(-1) if k_scale.dim() == 3 else k_scale
+    seq_stride = kc.stride(0) // DIM
+    _need(ks.dtype == torch.float32 and ks.dim() == 2 and ks.shape[:2] == kc.shape[:2] and ks.stride(1) == 1
+          and (ks.shape[0] == 1 or ks.stride(0) == seq_stride), "k_scale must share k_cache's sequence stride")
+    _need(0 <= T <= kc.shape[1], "T exceeds the cache capacity")
+    if scores is None:
+        scores = torch.empty((B, 1, T), dtype=torch.float32, device=q.device)
+    _need(scores.dtype == torch.float32 and scores.numel() == B * T and scores.is_contiguous(), "bad scores")
+    q8p = wep = None
+    if q_fp8_out is not None or w_eff_out is not None:
+        _need(q_fp8_out is not None and w_eff_out is not None, "pass both q_fp8_out and w_eff_out, or neither")
+        q8o = _byte_view(q_fp8_out)
+        _need(q8o.dtype == torch.uint8 and q8o.numel() == B * H * DIM and q8o.is_contiguous(), "bad q_fp8_out")
+        _need(w_eff_out.dtype == torch.float32 and w_eff_out.numel() == B * H and w_eff_out.is_contiguous(),
+              "bad w_eff_out")
+        q8p, wep = q8o.data_ptr(), w_eff_out.data_ptr()
+    rows = _rows(B, 1, T, start_pos, seq_len, causal)
+    st = _lib.load().lk_decode_score(q.data_ptr(), w.data_ptr(), H, k_new.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                     seq_stride, ctypes.byref(rows), scores.data_ptr(), q8p, wep, _stream(q))
+    _lib.check("lk_decode_score", st)
+    return scores
+
+
 def lk_topk(scores: torch.Tensor, k: int, start_pos: int = 0, seq_len: Optional[torch.Tensor] = None,
             causal: bool = False, idx: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Indices [B, S, k] (int32) of the min(k, L) largest scores of each row's valid

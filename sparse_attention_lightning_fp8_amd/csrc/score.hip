@@ -19,6 +19,7 @@
 // 32m + 8(i/4) + 4(l/32) + (i%4) for i < 16, so a lane sums 32 heads in registers and
 // one cross-half swap (v_permlane32_swap) completes the 64-head sum.
 #include "lk_device.h"
+#include "quant_device.h"
 
 namespace lk {
 namespace {
@@ -104,42 +105,110 @@ __device__ __forceinline__ float score_tile(const uint4 kv[4], const QueryFrag &
 
 // ------------------------------------------------------------------ decode (S == 1)
 // One wave scores 128 consecutive keys (4 tiles of 32) of one query row; a block of
-// 4 waves covers 512 keys.  Each lane loads its 4 x 64 bytes of K straight into the
-// B-operand registers (keys are read exactly once, so LDS brings no reuse here).
-// Order of work: the small query/weight loads first (L2 hits), then every K load of
-// the wave (16 KB in flight), then the query conversion while K streams in, then the
-// tiles in arrival order, so compute overlaps the HBM stream.
-constexpr int kDecWaves = 4;
+// kDecWaves waves covers kDecKeysPerBlock keys of that row.  Each lane loads its
+// 4 x 64 bytes of K straight into the B-operand registers (keys are read exactly
+// once, so staging K in LDS brings no reuse).  The query (8 KB as e4m3fn) and its
+// weights (256 B) are needed by every wave: the block fetches them once into LDS and
+// each wave takes its A fragments from there.
+// Order of work: the query loads, then every K load of the wave (16 KB in flight),
+// then the query staging while K streams in, then the tiles in arrival order.
+//
+// The fused variant (lk_decode_score) starts from the bf16 query, the raw weights
+// and the new key of the decode step: each block quantizes the row's 64 query heads
+// itself (8 lanes per head, the same arithmetic as lk_quantize_queries) while its K
+// loads are in flight, and the block holding key L-1 (the new token's slot) also
+// rotates and quantizes the new key, writes it to the cache, and hands it to the
+// lanes that score it in place of the stale cache row they loaded.
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecTiles = 4;                       // 32-key tiles per wave
 constexpr int kDecKeysPerWave = 32 * kDecTiles;    // 128
 constexpr int kDecKeysPerBlock = kDecKeysPerWave * kDecWaves;
+constexpr int kQPitch = LK_DIM + 16;               // LDS row pitch of the staged query (spreads banks)
+static_assert(LK_HEADS * LK_DIM / 16 == kDecThreads, "one 16-byte query piece per thread");
+static_assert(LK_HEADS * 8 == kDecThreads, "one 8-lane row group per head");
 
-__global__ void __launch_bounds__(256)
-score_decode_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict__ w_eff,
-                    const uint8_t *__restrict__ k_cache, const float *__restrict__ k_scale,
-                    int64_t cache_seq_stride, RowsDev rows, float *__restrict__ scores) {
+struct DecodeArgs {
+    const uint8_t *q_fp8;       // [B, 64, 128] e4m3fn        (standalone score)
+    const float *w_eff;         // [B, 64] folded weights     (standalone score)
+    const uint16_t *q_bf16;     // [B, 64, 128] bf16          (fused)
+    const float *w;             // [B, 64] raw weights        (fused)
+    const uint16_t *k_new;      // [B, 128] bf16 new keys     (fused)
+    uint8_t *q_fp8_out;         // optional copies of the quantized query (fused)
+    float *w_eff_out;
+    uint8_t *k_cache;           // [B, stride, 128]; the fused kernel writes row L-1
+    float *k_scale;             // [B, stride]
+    int64_t cache_seq_stride;
+    RowsDev rows;
+    float *scores;              // [B, T]
+};
+
+template <bool kFused>
+__global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t sq[LK_HEADS * kQPitch];
+    __shared__ __attribute__((aligned(16))) float sw[LK_HEADS];
+    __shared__ __attribute__((aligned(16))) uint4 snew[8];   // fused: the new key's 128 codes
+    __shared__ float snew_scale;
     const int lane = __lane_id();
     const int wave = threadIdx.x >> 6;
     const int qrow = blockIdx.y;                       // b * S + t  (S == 1)
-    const int b = qrow / rows.S;
-    const int t = qrow - b * rows.S;
-    const int64_t T = rows.T;
-    const int64_t L = row_len(rows, b, t);
-    const int64_t key0 = (int64_t)blockIdx.x * kDecKeysPerBlock + (int64_t)wave * kDecKeysPerWave;
-    if (key0 >= T) return;
-    float *out = scores + (int64_t)qrow * T;
-    if (key0 >= L) {                                   // fully masked: -inf only
-#pragma unroll
-        for (int p = 0; p < kDecTiles / 2; p++) {
-            const int64_t s = key0 + 64 * p + lane;
-            if (s < T) out[s] = -__builtin_inff();
+    const int b = qrow / a.rows.S;
+    const int t = qrow - b * a.rows.S;
+    const int64_t T = a.rows.T;
+    const int64_t L = row_len(a.rows, b, t);
+    const int64_t blk0 = (int64_t)blockIdx.x * kDecKeysPerBlock;
+    const int64_t key0 = blk0 + (int64_t)wave * kDecKeysPerWave;
+    float *out = a.scores + (int64_t)qrow * T;
+    const int head = threadIdx.x >> 3, sub = threadIdx.x & 7;   // fused: this thread's 16 features of a head
+    if (blk0 >= L) {                                   // the whole block is masked: -inf only
+        for (int64_t s = blk0 + threadIdx.x; s < blk0 + kDecKeysPerBlock && s < T; s += kDecThreads)
+            out[s] = -__builtin_inff();
+        if constexpr (kFused) {                        // a row with L == 0 still returns its quantized query
+            if (blockIdx.x == 0 && a.q_fp8_out) {
+                const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
+                const uint4 q0 = qs[0], q1 = qs[1];
+                uint32_t in[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                uint32_t codes[4];
+                int j;
+                quantize_row16(in, codes, j);
+                *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) =
+                    make_uint4(codes[0], codes[1], codes[2], codes[3]);
+                if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = fold_weight(a.w[(int64_t)qrow * LK_HEADS + head], j);
+            }
         }
         return;
     }
     const int r = lane & 31, hh = lane >> 5;
-    QueryRaw raw;
-    load_query_raw(q_fp8 + (int64_t)qrow * LK_HEADS * LK_DIM, w_eff + (int64_t)qrow * LK_HEADS, lane, raw);
-    const uint8_t *kbase = k_cache + (int64_t)b * cache_seq_stride * LK_DIM;
+    const int64_t pn = L - 1;                          // fused: the new key's slot
+    const bool has_new = kFused && pn < blk0 + kDecKeysPerBlock;
+
+    // Query, weights and (fused) new-key loads, issued before the K loads and never
+    // under a branch, so the waits of the staging below count the K loads exactly.
+    uint4 qp0, qp1, kn0, kn1;
+    float4 wv;
+    float wr = 0.f;
+    if constexpr (kFused) {
+        const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
+        qp0 = qs[0];
+        qp1 = qs[1];
+        wr = a.w[(int64_t)qrow * LK_HEADS + head];
+        const uint4 *kns = reinterpret_cast<const uint4 *>(a.k_new + (int64_t)b * LK_DIM + 16 * sub);
+        kn0 = kns[0];
+        kn1 = kns[1];
+    } else {
+        qp0 = reinterpret_cast<const uint4 *>(a.q_fp8 + (int64_t)qrow * LK_HEADS * LK_DIM)[threadIdx.x];
+        // Every thread loads and stores a float4 of the weights (lane % 16 picks which).
+        wv = reinterpret_cast<const float4 *>(a.w_eff + (int64_t)qrow * LK_HEADS)[lane & 15];
+    }
+    // Key scales before the K loads: the first tile pair's store needs them, and a
+    // load issued after the K loads could only be waited for together with all of K.
+    float ks[kDecTiles / 2];
+#pragma unroll
+    for (int p = 0; p < kDecTiles / 2; p++) {
+        const int64_t s = key0 + 64 * p + lane;
+        ks[p] = a.k_scale[(int64_t)b * a.cache_seq_stride + (s < L ? s : 0)];
+    }
+    const uint8_t *kbase = a.k_cache + (int64_t)b * a.cache_seq_stride * LK_DIM;
     uint4 kv[kDecTiles][4];
 #pragma unroll
     for (int j = 0; j < kDecTiles; j++) {
@@ -148,19 +217,71 @@ score_decode_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict__
 #pragma unroll
         for (int c = 0; c < 4; c++) kv[j][c] = src[c];       // rows past L re-read row 0 (masked below)
     }
-    float ks[kDecTiles / 2];
-#pragma unroll
-    for (int p = 0; p < kDecTiles / 2; p++) {
-        const int64_t s = key0 + 64 * p + lane;
-        ks[p] = k_scale[(int64_t)b * cache_seq_stride + (s < L ? s : 0)];
-    }
     // Keep every load above this point: all of the wave's K bytes must be in flight
-    // before any compute, or the stream stalls behind the MFMA work.
+    // before the staging waits for its own loads.
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kFused) {
+        uint32_t in[8] = {qp0.x, qp0.y, qp0.z, qp0.w, qp1.x, qp1.y, qp1.z, qp1.w};
+        uint32_t codes[4];
+        int j;
+        quantize_row16(in, codes, j);
+        const uint4 piece = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+        *reinterpret_cast<uint4 *>(sq + head * kQPitch + 16 * sub) = piece;
+        const float we = fold_weight(wr, j);
+        if (sub == 0) sw[head] = we;
+        if (blockIdx.x == 0 && a.q_fp8_out) {
+            *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) = piece;
+            if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = we;
+        }
+        if (has_new && wave == 0) {                    // all 8 row groups of wave 0 compute the same key
+            uint32_t kin[8] = {kn0.x, kn0.y, kn0.z, kn0.w, kn1.x, kn1.y, kn1.z, kn1.w};
+            uint32_t kc[4];
+            int kj;
+            quantize_row16(kin, kc, kj);
+            if (lane < 8) {
+                const uint4 kpiece = make_uint4(kc[0], kc[1], kc[2], kc[3]);
+                const int64_t row = (int64_t)b * a.cache_seq_stride + pn;
+                *reinterpret_cast<uint4 *>(a.k_cache + row * LK_DIM + 16 * sub) = kpiece;
+                snew[sub] = kpiece;
+                if (sub == 0) {
+                    const float ksc = __builtin_ldexpf(1.0f, kj);
+                    a.k_scale[row] = ksc;
+                    snew_scale = ksc;
+                }
+            }
+        }
+    } else {
+        const int piece = threadIdx.x;                 // head piece / 8, 16-byte chunk piece % 8
+        *reinterpret_cast<uint4 *>(sq + (piece >> 3) * kQPitch + 16 * (piece & 7)) = qp0;
+        reinterpret_cast<float4 *>(sw)[lane & 15] = wv;    // duplicate stores of equal values
+    }
+    __syncthreads();
+    // A wave whose keys are all masked still runs the tiles (on re-read row 0) and
+    // stores -inf: a branch here would let the compiler sink the K loads below the
+    // barrier.  Only blocks that straddle a row's end have such waves.
+    QueryRaw raw;
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const uint8_t *qr = sq + (32 * m + r) * kQPitch + 64 * hh;
+#pragma unroll
+        for (int c = 0; c < 4; c++) raw.q[m][c] = *reinterpret_cast<const uint4 *>(qr + 16 * c);
+#pragma unroll
+        for (int g = 0; g < 4; g++) raw.w[m][g] = *reinterpret_cast<const float4 *>(sw + 32 * m + 8 * g + 4 * hh);
+    }
     QueryFrag f;
     convert_query(raw, f);
 #pragma unroll
     for (int p = 0; p < kDecTiles / 2; p++) {
+        if (has_new) {                                 // the lanes holding the new key take the fresh codes
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++) {
+                if (key0 + 32 * (2 * p + h2) + r == pn) {
+#pragma unroll
+                    for (int c = 0; c < 4; c++) kv[2 * p + h2][c] = snew[4 * hh + c];
+                }
+            }
+            if (key0 + 64 * p + lane == pn) ks[p] = snew_scale;
+        }
         const float p0 = score_tile(kv[2 * p], f);
         const float p1 = score_tile(kv[2 * p + 1], f);
         // lanes 0-31: tile 2p, key l; lanes 32-63: tile 2p+1, key l-32  ->  key key0 + 64p + l
@@ -266,15 +387,42 @@ hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const ui
                               const float *k_scale, int64_t cache_seq_stride, const RowsDev &rows,
                               float *scores, hipStream_t stream) {
     if (rows.S == 1) {
+        DecodeArgs a{};
+        a.q_fp8 = q_fp8;
+        a.w_eff = w_eff;
+        a.k_cache = const_cast<uint8_t *>(k_cache);    // read only: the standalone kernel never writes it
+        a.k_scale = const_cast<float *>(k_scale);
+        a.cache_seq_stride = cache_seq_stride;
+        a.rows = rows;
+        a.scores = scores;
         dim3 grid((unsigned)((rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock), (unsigned)rows.B);
-        return launch(score_decode_kernel, grid, dim3(64 * kDecWaves), 0u, stream, q_fp8, w_eff, k_cache,
-                      k_scale, cache_seq_stride, rows, scores);
+        return launch(decode_kernel<false>, grid, dim3(kDecThreads), 0u, stream, a);
     } else {
         dim3 grid((unsigned)((rows.T + kPreChunk - 1) / kPreChunk), (unsigned)((rows.S + kPreWaves - 1) / kPreWaves),
                   (unsigned)rows.B);
         return launch(score_prefill_kernel, grid, dim3(64 * kPreWaves), 0u, stream, q_fp8, w_eff, k_cache,
                       k_scale, cache_seq_stride, rows, scores);
     }
+}
+
+// The fused decode step: S == 1 rows, query quantization and the new key's write
+// done inside the score kernel.
+hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t *k_new, uint8_t *k_cache,
+                               float *k_scale, int64_t cache_seq_stride, const RowsDev &rows, float *scores,
+                               uint8_t *q_fp8_out, float *w_eff_out, hipStream_t stream) {
+    DecodeArgs a{};
+    a.q_bf16 = q;
+    a.w = w;
+    a.k_new = k_new;
+    a.q_fp8_out = q_fp8_out;
+    a.w_eff_out = w_eff_out;
+    a.k_cache = k_cache;
+    a.k_scale = k_scale;
+    a.cache_seq_stride = cache_seq_stride;
+    a.rows = rows;
+    a.scores = scores;
+    dim3 grid((unsigned)((rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock), (unsigned)rows.B);
+    return launch(decode_kernel<true>, grid, dim3(kDecThreads), 0u, stream, a);
 }
 
 }  // namespace lk

@@ -116,6 +116,36 @@ def gpu_pipeline(inp: W.Inputs, device="cuda:0", new_rows_only: bool = False) ->
     return GpuResult(cache, cache_scale, q_fp8, w_eff, q_scale, scores, idx)
 
 
+def gpu_pipeline_fused(inp: W.Inputs, device="cuda:0") -> GpuResult:
+    """The fused decode step through the C ABI: the cache prefix [0, L-1) of each
+    sequence is written first (slot L-1 and beyond hold 0xAA garbage), then one
+    lk_decode_score launch writes the new key at L-1, quantizes the query and scores,
+    then lk_topk."""
+    from sparse_attention_lightning_fp8_amd import api
+    wl = inp.wl
+    assert wl.S == 1
+    k = inp.k.to(device)
+    cache = torch.full((wl.B, wl.cap, 128), 0xAA, dtype=torch.uint8, device=device)
+    cache_scale = torch.full((wl.B, wl.cap), 3.0, dtype=torch.float32, device=device)
+    seq_len = inp.lens.to(device) if inp.lens is not None else None
+    new_rows = k.new_empty((wl.B, 128))
+    for b in range(wl.B):
+        sl = int(inp.lens[b]) if inp.lens is not None else -1
+        L = O.valid_len(wl.T, sl, wl.causal, wl.start_pos, 0)
+        if L > 1:
+            api.lk_quantize_keys(k[b:b + 1, :L - 1], cache[b:b + 1], cache_scale[b:b + 1])
+        new_rows[b] = k[b, max(L - 1, 0)]
+    q = inp.q.to(device).reshape(wl.B, 64, 128)
+    w = inp.w.to(device).reshape(wl.B, 64)
+    q_fp8 = torch.empty((wl.B, 1, 64, 128), dtype=torch.uint8, device=device)
+    w_eff = torch.empty((wl.B, 1, 64), dtype=torch.float32, device=device)
+    scores = api.lk_decode_score(q, w, new_rows, cache, cache_scale, wl.T, start_pos=wl.start_pos,
+                                 seq_len=seq_len, causal=wl.causal, q_fp8_out=q_fp8, w_eff_out=w_eff)
+    idx = api.lk_topk(scores, wl.k, start_pos=wl.start_pos, seq_len=seq_len, causal=wl.causal)
+    torch.cuda.synchronize()
+    return GpuResult(cache, cache_scale, q_fp8, w_eff, None, scores, idx)
+
+
 # ------------------------------------------------------------------ comparisons
 def compare_scores(gpu_rows: List[np.ndarray], ref_rows: List[OracleRow]) -> float:
     """Assert the -inf pattern is exact and finite entries agree within tolerance.

@@ -28,7 +28,8 @@ def lib():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     assert syms == sorted(["lk_quantize_keys", "lk_quantize_queries", "lk_index_score", "lk_topk",
-                           "lk_prepare", "lk_profile_next_launch", "lk_status_string", "lk_abi_version"])
+                           "lk_prepare", "lk_decode_score", "lk_profile_next_launch", "lk_status_string",
+                           "lk_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -101,6 +102,25 @@ def test_index_score_validation(lib):
     assert f(A, A, 64, A, A, 70000, rows(B=70000, T=16), A, None) == E_UNSUP  # grid limit
     assert f(None, None, 64, None, None, 16, rows(B=0), None, None) == OK
     assert f(None, None, 64, None, None, 16, rows(T=0), None, None) == OK
+
+
+def test_decode_score_validation(lib):
+    f = lib.lk_decode_score
+    #       q  w   H   kn k_cache k_scale stride rows      scores q8o  weo  stream
+    assert f(A, A, 64, A, A, A, 16, None, A, None, None, None) == E_NULL
+    assert f(A, A, 64, A, A, A, 16, rows(S=2), A, None, None, None) == E_SHAPE      # decode rows only
+    assert f(A, A, 64, A, A, A, 16, rows(T=17), A, None, None, None) == E_SHAPE     # T beyond the cache
+    assert f(A, A, 32, A, A, A, 16, rows(), A, None, None, None) == E_UNSUP         # heads != 64
+    assert f(A, A, 64, A, A, A, 16, rows(), A, A, None, None) == E_NULL             # one optional output
+    assert f(None, A, 64, A, A, A, 16, rows(), A, None, None, None) == E_NULL
+    assert f(A, A, 64, None, A, A, 16, rows(), A, None, None, None) == E_NULL
+    assert f(A, A, 64, A, A, A, 16, rows(), None, None, None, None) == E_NULL
+    assert f(A + 8, A, 64, A, A, A, 16, rows(), A, None, None, None) == E_UNSUP     # misaligned q
+    assert f(A, A, 64, A + 8, A, A, 16, rows(), A, None, None, None) == E_UNSUP     # misaligned k_new
+    assert f(A, A + 2, 64, A, A, A, 16, rows(), A, None, None, None) == E_UNSUP
+    assert f(A, A, 64, A, A, A, 16, rows(), A, A + 4, A, None) == E_UNSUP
+    assert f(A, A, 64, A, A, A, 70000, rows(B=70000, T=16), A, None, None, None) == E_UNSUP
+    assert f(None, None, 64, None, None, None, 16, rows(B=0), None, None, None, None) == OK
 
 
 def test_topk_validation(lib):
