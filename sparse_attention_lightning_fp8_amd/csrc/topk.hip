@@ -62,6 +62,15 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
     return x;
 }
 
+// Inclusive scan within each 16-lane DPP row; lane 16r + 15 ends with row r's sum.
+__device__ __forceinline__ uint32_t row_scan16(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    return x;
+}
+
 // Running maximum and minimum over the lanes of a wave, ignoring NaN lanes (lanes
 // that DPP cannot source read NaN, which fmaxf/fminf ignore); lane 63 ends with the
 // wave's result.
@@ -137,12 +146,14 @@ __device__ __forceinline__ uint32_t elem_index(int tid, int e) {
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *__restrict__ idx) {
     static_assert(kThreads * 4 == kBins && kThreads * kPer == LK_TOPK_MAX_T && kWaves == 16, "tiling");
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kBins + 4];   // + a spare word for invalid elements
+    __shared__ __attribute__((aligned(16))) uint32_t hist_buf[4 + kBins];   // word 3: invalid elements
+    uint32_t *const hist = hist_buf + 4;                                     // bins 0 .. kBins-1
     __shared__ uint32_t wtot[4][kWaves];
     __shared__ uint32_t wsum[kWaves];
     __shared__ float wred[2][kWaves];
     __shared__ uint32_t sel[3];
-    __shared__ uint32_t cand_key[kSmall], cand_idx[kSmall];
+    __shared__ __attribute__((aligned(16))) uint32_t cand_key[kSmall];
+    __shared__ __attribute__((aligned(16))) uint32_t cand_idx[kSmall];
     __shared__ uint32_t ccount, cut[2];
 
     const int row = blockIdx.x;
@@ -212,15 +223,20 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
     const bool spread = width >= 1e-30f && width <= 1e30f;
     // scale = 4095 / width keeps (mx - mn) * scale below 4096 despite rounding, and
     // every valid score of a spread row is finite, so bins are 0 .. 4095.
-    const float lo = spread ? mn : 0.f, scale = spread ? 4095.f / width : 0.f;
-    auto bin_of = [&](float x) -> uint32_t { return spread ? (uint32_t)((x - lo) * scale) : 0u; };
+    const float scale = 4095.f / width;
+    // Bin of element e, -1 for an invalid (NaN) element: fmaxf returns -1 for NaN.  A
+    // row without spread puts every valid element in bin 0.
+    auto bin_of = [&](int e) -> int {
+        if (spread) return (int)fmaxf((v[e] - mn) * scale, -1.0f);
+        return v[e] == v[e] ? 0 : -1;
+    };
 
-    // 2-3. Histogram of the bins, then the bin holding the k-th largest.
+    // 2-3. Histogram of the bins (invalid elements count in hist[-1], a spare word),
+    //      then the bin holding the k-th largest.
 #pragma unroll
     for (int e = 0; e < kPer; e++) {
         if (!live(e >> 2)) continue;
-        const bool ok = v[e] == v[e];                  // invalid elements count in the spare word
-        atomicAdd(&hist[ok ? bin_of(v[e]) : (uint32_t)kBins], 1u);
+        atomicAdd(&hist[bin_of(e)], 1u);
     }
     __syncthreads();
     select_bin(hist, (uint32_t)k, wsum, sel);
@@ -232,10 +248,9 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
 #pragma unroll
     for (int e = 0; e < kPer; e++) {
         if (!live(e >> 2)) continue;
-        const uint32_t bn = bin_of(v[e]);
-        const bool ok = v[e] == v[e];
-        gbits |= (ok && bn > cb ? 1u : 0u) << e;
-        ebits |= (ok && bn == cb ? 1u : 0u) << e;
+        const int bn = bin_of(e);                      // -1 (invalid) is never > or == cb
+        gbits |= (bn > (int)cb ? 1u : 0u) << e;
+        ebits |= (bn == (int)cb ? 1u : 0u) << e;
     }
     // The cut inside bin cb: of its elements, those whose key & pmask exceeds prefix
     // join gbits, and the `need` lowest-index ones whose key & pmask equals prefix
@@ -249,18 +264,33 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
             cand_idx[slot] = elem_index(tid, e);
         }
         __syncthreads();
-        if (wave == 0) {
-            const uint32_t mk = lane < (int)cnt ? cand_key[lane] : 0u, mi = lane < (int)cnt ? cand_idx[lane] : 0u;
-            uint32_t gt = 0, eq_before = 0;
-            for (uint32_t j = 0; j < cnt; j++) {
-                const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)j);
-                const uint32_t ij = (uint32_t)__builtin_amdgcn_readlane((int)mi, (int)j);
-                gt += kj > mk ? 1u : 0u;
-                eq_before += (kj == mk && ij < mi) ? 1u : 0u;
+        // Rank of candidate ci = tid / 16 among all candidates (score descending, index
+        // ascending): the 16 lanes of a DPP row each compare it with 4 candidates and
+        // the row sums the packed counts (above: low half, equal with a lower index: high).
+        {
+            const int ci = tid >> 4, q = tid & 15;
+            uint32_t packed = 0, mk = 0, mi = 0;
+            if (ci < (int)cnt) {
+                mk = cand_key[ci];
+                mi = cand_idx[ci];
+                const uint4 kq = *reinterpret_cast<const uint4 *>(cand_key + 4 * q);
+                const uint4 iq = *reinterpret_cast<const uint4 *>(cand_idx + 4 * q);
+                const uint32_t kj[4] = {kq.x, kq.y, kq.z, kq.w}, ij[4] = {iq.x, iq.y, iq.z, iq.w};
+#pragma unroll
+                for (int jj = 0; jj < 4; jj++) {
+                    if (4 * q + jj < (int)cnt) {
+                        packed += kj[jj] > mk ? 1u : 0u;
+                        packed += (kj[jj] == mk && ij[jj] < mi) ? 0x10000u : 0u;
+                    }
+                }
             }
-            if (lane < (int)cnt && gt + eq_before == need - 1) {   // the need-th candidate: the cut
-                cut[0] = mk;
-                cut[1] = need - gt;
+            packed = row_scan16(packed);
+            if (q == 15 && ci < (int)cnt) {
+                const uint32_t gt = packed & 0xFFFFu, eq_before = packed >> 16;
+                if (gt + eq_before == need - 1) {      // the need-th candidate: the cut
+                    cut[0] = mk;
+                    cut[1] = need - gt;
+                }
             }
         }
         __syncthreads();
