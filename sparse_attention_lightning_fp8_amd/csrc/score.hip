@@ -79,12 +79,13 @@ __device__ __forceinline__ void load_query(const uint8_t *__restrict__ q_row, co
 // Scores are finite by contract, so ReLU is a single v_max (the file is built
 // without NaN semantics).
 __device__ __forceinline__ float relu_weighted_sum(const float16v acc[2], const QueryFrag &f) {
-    float s = 0.0f;
+    // Four independent partial sums, so consecutive FMAs do not wait on each other.
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int m = 0; m < 2; m++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) s = __builtin_fmaf(__builtin_fmaxf(acc[m][i], 0.0f), f.w[m][i], s);
-    return s;
+        for (int i = 0; i < 16; i++) s[i & 3] = __builtin_fmaf(__builtin_fmaxf(acc[m][i], 0.0f), f.w[m][i], s[i & 3]);
+    return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
 // Scores of one 32-key tile whose B operand (this lane's 64 bytes of key l % 32) is `kv`.
@@ -292,26 +293,70 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ prefill (S > 1)
-// A block of 8 waves owns 8 consecutive query tokens of one sequence (one per wave)
-// and a chunk of 256 keys.  The chunk is read from HBM once per block, converted to
-// f16 once, and kept in LDS; every wave then streams it through the MFMA against
-// its own query held in registers.
-constexpr int kPreWaves = 8;
-constexpr int kPreChunk = 256;                      // keys per block
+// A block of 4 waves (one per SIMD) owns 4 consecutive query tokens of one sequence
+// (one per wave) and a slice of 2048 keys, taken as sixteen chunks of 128.  Each
+// chunk is read from HBM once per block, converted to f16 once and kept in LDS, where
+// every wave streams it through the MFMA against its own query held in registers.
+// The chunks are double buffered: the loads of chunk c+1 are issued before chunk c's
+// MFMA work and land in the other LDS buffer after it, and the query is loaded and
+// converted once per slice.  Two blocks share a CU (70 KB of LDS each), so each SIMD
+// runs one wave of each: the two never meet at a barrier, and one block's prologue
+// and chunk hand-overs are covered by the other block's MFMA work.  (With both waves
+// of a SIMD in one block, the issue arbiter's preference for the older wave made the
+// younger one finish each chunk ~40% later while the block waited at the barrier.)
+constexpr int kPreWaves = 4;
+constexpr int kPreThreads = 64 * kPreWaves;
+constexpr int kPreChunk = 128;                      // keys per LDS buffer
+constexpr int kPreChunks = 16;                      // chunks per block
+constexpr int kPreSlice = kPreChunk * kPreChunks;   // keys per block
 constexpr int kPreRowBytes = 2 * LK_DIM + 16;       // f16 row + 16 B pad against bank conflicts
+static_assert(kPreThreads == 2 * kPreChunk, "two threads stage each key row");
 
-__global__ void __launch_bounds__(512)
+// One thread's share of a chunk in flight: half a key row (64 fp8 bytes) and, for
+// threads below kPreChunk, one key scale.
+struct ChunkPart {
+    uint4 v[4];
+    float ks;
+};
+
+__device__ __forceinline__ void load_chunk_part(const uint8_t *__restrict__ kbase, const float *__restrict__ sbase,
+                                                int64_t kc, int64_t Lmax, ChunkPart &p) {
+    const int kr = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int64_t s = kc + kr;
+    if (s < Lmax) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(kbase + s * LK_DIM + 64 * half);
+#pragma unroll
+        for (int c = 0; c < 4; c++) p.v[c] = src[c];
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; c++) p.v[c] = make_uint4(0, 0, 0, 0);
+    }
+    p.ks = (threadIdx.x < kPreChunk && kc + threadIdx.x < Lmax) ? sbase[kc + threadIdx.x] : 0.0f;
+}
+
+__device__ __forceinline__ void store_chunk_part(uint8_t *sk, float *sks, const ChunkPart &p) {
+    const int kr = threadIdx.x >> 1, half = threadIdx.x & 1;
+    half8 *dst = reinterpret_cast<half8 *>(sk + kr * kPreRowBytes + 128 * half);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        dst[2 * c] = fp8x8_to_half8(p.v[c].x, p.v[c].y);
+        dst[2 * c + 1] = fp8x8_to_half8(p.v[c].z, p.v[c].w);
+    }
+    if (threadIdx.x < kPreChunk) sks[threadIdx.x] = p.ks;
+}
+
+__global__ void __launch_bounds__(kPreThreads)
 score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict__ w_eff,
                      const uint8_t *__restrict__ k_cache, const float *__restrict__ k_scale,
                      int64_t cache_seq_stride, RowsDev rows, float *__restrict__ scores) {
-    __shared__ __attribute__((aligned(16))) uint8_t sk[kPreChunk * kPreRowBytes];
-    __shared__ float sks[kPreChunk];
+    __shared__ __attribute__((aligned(16))) uint8_t sk[2][kPreChunk * kPreRowBytes];
+    __shared__ float sks[2][kPreChunk];
     const int lane = __lane_id();
     const int wave = threadIdx.x >> 6;
     const int b = blockIdx.z;
     const int t0 = blockIdx.y * kPreWaves;
     const int64_t T = rows.T;
-    const int64_t kc0 = (int64_t)blockIdx.x * kPreChunk;
+    const int64_t slice0 = (int64_t)blockIdx.x * kPreSlice;
     const int t = t0 + wave;
     const bool has_row = t < rows.S;
     const int64_t L = has_row ? row_len(rows, b, t) : 0;
@@ -319,65 +364,104 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
     const int t_last = (t0 + kPreWaves - 1 < rows.S ? t0 + kPreWaves - 1 : rows.S - 1);
     const int64_t Lmax = row_len(rows, b, t_last);     // row_len is non-decreasing in t
     float *out = scores + ((int64_t)b * rows.S + t) * T;
-    if (kc0 >= Lmax) {                                  // whole block masked
-        if (has_row)
-            for (int64_t s = kc0 + lane; s < kc0 + kPreChunk && s < T; s += 64) out[s] = -__builtin_inff();
-        return;
-    }
-    // Stage the chunk: thread i converts half of key (i / 2) to f16.
-    {
-        const int kr = threadIdx.x >> 1, half = threadIdx.x & 1;
-        const int64_t s = kc0 + kr;
-        uint4 v[4];
-        if (s < Lmax) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(
-                k_cache + ((int64_t)b * cache_seq_stride + s) * LK_DIM + 64 * half);
-#pragma unroll
-            for (int c = 0; c < 4; c++) v[c] = src[c];
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; c++) v[c] = make_uint4(0, 0, 0, 0);
-        }
-        half8 *dst = reinterpret_cast<half8 *>(sk + kr * kPreRowBytes + 128 * half);
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            dst[2 * c] = fp8x8_to_half8(v[c].x, v[c].y);
-            dst[2 * c + 1] = fp8x8_to_half8(v[c].z, v[c].w);
-        }
-        if (threadIdx.x < kPreChunk)
-            sks[threadIdx.x] = (kc0 + threadIdx.x < Lmax)
-                                   ? k_scale[(int64_t)b * cache_seq_stride + kc0 + threadIdx.x] : 0.0f;
-    }
+    // Chunks of the slice with any valid key for some row of the block.
+    const int64_t live = Lmax - slice0;
+    const int nchunks = live <= 0 ? 0 : (live >= kPreSlice ? kPreChunks : (int)((live + kPreChunk - 1) / kPreChunk));
+    // -inf for this row's slots of the chunks no row of the block needs.
+    if (has_row)
+        for (int64_t s = slice0 + (int64_t)nchunks * kPreChunk + lane; s < slice0 + kPreSlice && s < T; s += 64)
+            out[s] = -__builtin_inff();
+    if (nchunks == 0) return;
+
+    const uint8_t *kbase = k_cache + (int64_t)b * cache_seq_stride * LK_DIM;
+    const float *sbase = k_scale + (int64_t)b * cache_seq_stride;
+    ChunkPart part;
+    load_chunk_part(kbase, sbase, slice0, Lmax, part);
     QueryFrag f;
     if (has_row) {
         const int64_t qrow = (int64_t)b * rows.S + t;
         load_query(q_fp8 + qrow * LK_HEADS * LK_DIM, w_eff + qrow * LK_HEADS, lane, f);
     }
+    store_chunk_part(sk[0], sks[0], part);
     __syncthreads();
-    if (!has_row) return;
     const int r = lane & 31, hh = lane >> 5;
-    for (int j = 0; j < kPreChunk / 32; j += 2) {
-        if (kc0 + 32 * j >= L) {                        // rest of the row is masked
-            for (int64_t s = kc0 + 32 * j + lane; s < kc0 + kPreChunk && s < T; s += 64) out[s] = -__builtin_inff();
-            break;
-        }
-        float part[2];
+    for (int c = 0; c < nchunks; c++) {
+        const int64_t kc = slice0 + (int64_t)c * kPreChunk;
+        const bool more = c + 1 < nchunks;
+        if (more) load_chunk_part(kbase, sbase, kc + kPreChunk, Lmax, part);   // in flight during the MFMA work
+        const uint8_t *skc = sk[c & 1];
+        const float *sksc = sks[c & 1];
+        if (has_row && kc + kPreChunk <= L) {
+            // Every key of the chunk is valid for this row: a software pipeline in which
+            // the MFMA chain of tile j+1 is issued before the ReLU / weighted-sum epilogue
+            // of tile j, so the VALU epilogue runs in the shadow of the matrix core.
+            const uint8_t *rowbase = skc + r * kPreRowBytes + 128 * hh;
+            auto mfma_tile = [&](int j, float16v acc[2]) {
+                acc[0] = float16v{};
+                acc[1] = float16v{};
 #pragma unroll
-        for (int jj = 0; jj < 2; jj++) {
-            const uint8_t *row = sk + (32 * (j + jj) + r) * kPreRowBytes + 128 * hh;
-            float16v acc[2] = {};
+                for (int kk = 0; kk < 8; kk++) {
+                    const half8 bk = *reinterpret_cast<const half8 *>(rowbase + 32 * j * kPreRowBytes + 16 * kk);
 #pragma unroll
-            for (int kk = 0; kk < 8; kk++) {
-                const half8 bk = *reinterpret_cast<const half8 *>(row + 16 * kk);
+                    for (int m = 0; m < 2; m++)
+                        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][kk], bk, acc[m], 0, 0, 0);
+                }
+            };
+            float16v acc[2][2];
+            float p[2];
+            mfma_tile(0, acc[0]);
 #pragma unroll
-                for (int m = 0; m < 2; m++)
-                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][kk], bk, acc[m], 0, 0, 0);
+            for (int j = 0; j < kPreChunk / 32; j++) {
+                // One scheduling region per stage: the next tile's 8 operand reads first,
+                // then part of this tile's epilogue while they land, then the MFMA chain
+                // interleaved with the rest of the epilogue (two MFMAs, six VALU ops per
+                // K-step).
+                __builtin_amdgcn_sched_barrier(0);
+                if (j + 1 < kPreChunk / 32) mfma_tile(j + 1, acc[(j + 1) & 1]);
+                p[j & 1] = relu_weighted_sum(acc[j & 1], f);
+                if (j & 1) {
+                    const float sum = halves_sum_pair(p[0], p[1]);
+                    const int64_t s = kc + 32 * (j - 1) + lane;
+                    out[s] = sum * sksc[32 * (j - 1) + lane];   // s < L <= T
+                }
+                if (j + 1 < kPreChunk / 32) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);       // the tile's 8 operand reads
+                    __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);      // VALU while they land
+#pragma unroll
+                    for (int kk = 0; kk < 8; kk++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+                    }
+                }
             }
-            part[jj] = relu_weighted_sum(acc, f);
+            __builtin_amdgcn_sched_barrier(0);
+        } else if (has_row) {
+            for (int j = 0; j < kPreChunk / 32; j += 2) {
+                if (kc + 32 * j >= L) {                // rest of this chunk is masked for the row
+                    for (int64_t s = kc + 32 * j + lane; s < kc + kPreChunk && s < T; s += 64) out[s] = -__builtin_inff();
+                    break;
+                }
+                float partial[2];
+#pragma unroll
+                for (int jj = 0; jj < 2; jj++) {
+                    const uint8_t *row = skc + (32 * (j + jj) + r) * kPreRowBytes + 128 * hh;
+                    float16v acc[2] = {};
+#pragma unroll
+                    for (int kk = 0; kk < 8; kk++) {
+                        const half8 bk = *reinterpret_cast<const half8 *>(row + 16 * kk);
+#pragma unroll
+                        for (int m = 0; m < 2; m++)
+                            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][kk], bk, acc[m], 0, 0, 0);
+                    }
+                    partial[jj] = relu_weighted_sum(acc, f);
+                }
+                const float sum = halves_sum_pair(partial[0], partial[1]);
+                const int64_t s = kc + 32 * j + lane;
+                if (s < T) out[s] = s < L ? sum * sksc[32 * j + lane] : -__builtin_inff();
+            }
         }
-        const float sum = halves_sum_pair(part[0], part[1]);
-        const int64_t s = kc0 + 32 * j + lane;
-        if (s < T) out[s] = s < L ? sum * sks[32 * j + lane] : -__builtin_inff();
+        if (more) store_chunk_part(sk[(c + 1) & 1], sks[(c + 1) & 1], part);
+        __syncthreads();
     }
 }
 
@@ -398,9 +482,9 @@ hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const ui
         dim3 grid((unsigned)((rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock), (unsigned)rows.B);
         return launch(decode_kernel<false>, grid, dim3(kDecThreads), 0u, stream, a);
     } else {
-        dim3 grid((unsigned)((rows.T + kPreChunk - 1) / kPreChunk), (unsigned)((rows.S + kPreWaves - 1) / kPreWaves),
+        dim3 grid((unsigned)((rows.T + kPreSlice - 1) / kPreSlice), (unsigned)((rows.S + kPreWaves - 1) / kPreWaves),
                   (unsigned)rows.B);
-        return launch(score_prefill_kernel, grid, dim3(64 * kPreWaves), 0u, stream, q_fp8, w_eff, k_cache,
+        return launch(score_prefill_kernel, grid, dim3(kPreThreads), 0u, stream, q_fp8, w_eff, k_cache,
                       k_scale, cache_seq_stride, rows, scores);
     }
 }
