@@ -38,6 +38,14 @@
  *   R9 top-k returns the min(k, L) largest scores of the valid prefix, ties to the
  *      lower index, -0 equal to +0, unused slots -1.
  *
+ *   R12 RoPE (Indexer.forward: "rope in indexer is not interleaved"; NKI page: RoPE
+ *      rotates the leading rope_dim features, cos and sin tables hold rope_dim/2
+ *      entries per token) rotates the pairs (i, i + h), h = rope_dim / 2, i < h:
+ *        y_i   = fl32( fl32(x_i c_i) - fl32(x_{i+h} s_i) ),
+ *        y_i+h = fl32( fl32(x_i s_i) + fl32(x_{i+h} c_i) ),
+ *      each then rounded to bf16 (nearest-even); features >= rope_dim are unchanged.
+ *      rope_dim is 64 for the indexer's 128-feature heads.
+ *
  * Parity with DeepSeek's own act_quant / fp8_index bytes is unpinned: the pages print
  * no numbers, so R1-R5 cannot be checked against the reference's outputs.
  *
@@ -261,6 +269,46 @@ int lko_quantize_rows(const uint16_t *x_bf16, int64_t n_rows, int d,
         int rc = lko_quantize_row(x_bf16 + r * d, d, codes + r * d, scales + r);
         if (rc != LKO_OK)
             return rc;
+    }
+    return LKO_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* RoPE on the leading features (reading R12).                                */
+/* ------------------------------------------------------------------------- */
+int lko_rope_row(const uint16_t *x_bf16, int d, int rope_dim, const float *cos_t,
+                 const float *sin_t, uint16_t *y_bf16)
+{
+    if (rope_dim < 0 || rope_dim > d || (rope_dim & 1)) return LKO_E_ARG;
+    const int h = rope_dim / 2;
+    for (int i = 0; i < d; i++) y_bf16[i] = x_bf16[i];
+    for (int i = 0; i < h; i++) {
+        const float a = (float)lko_bf16_decode(x_bf16[i]);
+        const float b = (float)lko_bf16_decode(x_bf16[i + h]);
+        const float ac = a * cos_t[i], bs = b * sin_t[i];
+        const float as = a * sin_t[i], bc = b * cos_t[i];
+        const float re = ac - bs, im = as + bc;
+        if (lko_bf16_round((double)re, &y_bf16[i]) != LKO_OK) return LKO_E_RANGE;
+        if (lko_bf16_round((double)im, &y_bf16[i + h]) != LKO_OK) return LKO_E_RANGE;
+    }
+    return LKO_OK;
+}
+
+/* RoPE then act_quant of many rows: x is [n_rows][d] bf16 and row r uses the cos/sin
+ * row (r / rows_per_table_row) of tables [*][rope_dim / 2]. */
+int lko_rope_quantize_rows(const uint16_t *x_bf16, int64_t n_rows, int d, int rope_dim,
+                           const float *cos_t, const float *sin_t, int64_t rows_per_table_row,
+                           uint8_t *codes, float *scales)
+{
+    uint16_t y[512];
+    if (d > 512 || rows_per_table_row < 1) return LKO_E_ARG;
+    for (int64_t r = 0; r < n_rows; r++) {
+        const int64_t tr = r / rows_per_table_row;
+        int rc = lko_rope_row(x_bf16 + r * d, d, rope_dim, cos_t + tr * (rope_dim / 2),
+                              sin_t + tr * (rope_dim / 2), y);
+        if (rc != LKO_OK) return rc;
+        rc = lko_quantize_row(y, d, codes + r * d, scales + r);
+        if (rc != LKO_OK) return rc;
     }
     return LKO_OK;
 }

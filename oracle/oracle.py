@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.lko_quantize_row.argtypes = [p, ctypes.c_int, p, p]
         L.lko_quantize_rows.argtypes = [p, i64, ctypes.c_int, p, p]
         L.lko_fold_weights.argtypes = [p, p, i64, ctypes.c_int, p]
+        L.lko_rope_row.argtypes = [p, ctypes.c_int, ctypes.c_int, p, p, p]
+        L.lko_rope_quantize_rows.argtypes = [p, i64, ctypes.c_int, ctypes.c_int, p, p, i64, p, p]
         L.lko_fold_weights.restype = None
         L.lko_valid_len.argtypes = [i64, i64, ctypes.c_int, i64, i64]
         L.lko_valid_len.restype = i64
@@ -135,6 +137,32 @@ def quantize_rows(x_bf16_bits: np.ndarray):
     codes = np.empty(x.shape, dtype=np.uint8)
     scales = np.empty(x.shape[:-1], dtype=np.float32)
     _check(lib().lko_quantize_rows(_ptr(x), n, d, _ptr(codes), _ptr(scales)), "quantize_rows")
+    return codes, scales
+
+
+def rope_row(x_bf16_bits: np.ndarray, cos_t: np.ndarray, sin_t: np.ndarray, rope_dim: int = 64) -> np.ndarray:
+    """RoPE on the leading rope_dim features of one bf16 row (reading R12); bf16 bits out."""
+    x = np.ascontiguousarray(x_bf16_bits, np.uint16)
+    c = np.ascontiguousarray(cos_t, np.float32)
+    s = np.ascontiguousarray(sin_t, np.float32)
+    assert c.size >= rope_dim // 2 and s.size >= rope_dim // 2
+    y = np.empty_like(x)
+    _check(lib().lko_rope_row(_ptr(x), x.size, rope_dim, _ptr(c), _ptr(s), _ptr(y)), "rope_row")
+    return y
+
+
+def rope_quantize_rows(x_bf16_bits: np.ndarray, cos_t: np.ndarray, sin_t: np.ndarray,
+                       rows_per_table_row: int = 1, rope_dim: int = 64):
+    """RoPE then act_quant of [n, 128] bf16 rows; row r uses table row r // rows_per_table_row."""
+    x = np.ascontiguousarray(x_bf16_bits, np.uint16).reshape(-1, 128)
+    n = x.shape[0]
+    c = np.ascontiguousarray(cos_t, np.float32).reshape(-1, rope_dim // 2)
+    s = np.ascontiguousarray(sin_t, np.float32).reshape(-1, rope_dim // 2)
+    assert c.shape[0] * rows_per_table_row >= n and s.shape == c.shape
+    codes = np.empty((n, 128), np.uint8)
+    scales = np.empty(n, np.float32)
+    _check(lib().lko_rope_quantize_rows(_ptr(x), n, 128, rope_dim, _ptr(c), _ptr(s), rows_per_table_row,
+                                        _ptr(codes), _ptr(scales)), "rope_quantize_rows")
     return codes, scales
 
 
