@@ -1,7 +1,8 @@
 """Benchmark of the lightning-indexer hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: key write of the step's new
-tokens, query rotate/quantize + weight fold, fp8 index score with mask, per-row top-k.
+A step is one pass of the whole path over one batch: RoPE, Hadamard rotation and fp8
+quantization of the step's new keys (written to the cache) and of the queries with the
+weight fold, fp8 index score with mask, per-row top-k.
 The step rate comes from an uninstrumented timed loop; per-kernel durations come from a
 second pass of the same steps with events recorded at each dispatch's start and end.
 The timed workload is decode with 16 sequences of 16384 cached keys (64 heads x 128,
@@ -76,6 +77,11 @@ class DecodeSet:
         self.scores = torch.empty((wl.B, wl.S, wl.T), dtype=torch.float32, device=dev)
         self.idx = torch.empty((wl.B, wl.S, wl.k), dtype=torch.int32, device=dev)
         self.seq_len = inp.lens.to(dev) if inp.lens is not None else None
+        # RoPE tables of the step's tokens (the new keys sit at the query positions)
+        from sparse_attention_lightning_fp8_amd import workloads as W
+        c, s = W.rope_tables(W.query_positions(inp).reshape(-1))
+        self.rope_tabs = (torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev))
+        self.k_rope = self.q_rope = (self.rope_tabs[0].data_ptr(), self.rope_tabs[1].data_ptr())
 
 
 def make_sets(api, inp, n_sets, dev):
@@ -108,7 +114,7 @@ def raw_calls(wl, s):
         (lib.lk_prepare, (s.k_new.data_ptr(), wl.B, wl.S, s.k_new.stride(0) // 128, s.cache.data_ptr(),
                           s.cache_scale.data_ptr(), cap, cap, 0, s.positions.data_ptr(),
                           s.q.data_ptr(), s.w.data_ptr(), wl.B * wl.S, 64, s.q8.data_ptr(),
-                          s.w_eff.data_ptr(), None, stream)),
+                          s.w_eff.data_ptr(), None, s.k_rope[0], s.k_rope[1], s.q_rope[0], s.q_rope[1], stream)),
         (lib.lk_index_score, (s.q8.data_ptr(), s.w_eff.data_ptr(), 64, s.cache.data_ptr(), s.cache_scale.data_ptr(),
                               cap, rows, s.scores.data_ptr(), stream)),
         (lib.lk_topk, (s.scores.data_ptr(), rows, wl.k, s.idx.data_ptr(), stream)),
@@ -128,7 +134,8 @@ def raw_calls_fused(wl, s):
     rows = ctypes.byref(s.rows)
     return [
         (lib.lk_decode_score, (s.q.data_ptr(), s.w.data_ptr(), 64, s.k_new.data_ptr(), s.cache.data_ptr(),
-                               s.cache_scale.data_ptr(), cap, rows, s.scores.data_ptr(), None, None, stream)),
+                               s.cache_scale.data_ptr(), cap, rows, s.scores.data_ptr(), None, None,
+                               s.q_rope[0], s.q_rope[1], stream)),
         (lib.lk_topk, (s.scores.data_ptr(), rows, wl.k, s.idx.data_ptr(), stream)),
     ]
 
@@ -191,14 +198,15 @@ def time_workload(api, wl_name, steps, warmup, n_sets, dev, fused=False):
 def fused_decode_bytes(wl, inp):
     """Bytes lk_decode_score must move for one step: per row, the cached keys [0, L-1)
     with their scales (132 B each), the new key (256 B of bf16 read, 132 B written),
-    every score slot (4 B), and the bf16 query with its weights (64 x 256 B + 64 x 4 B)."""
+    every score slot (4 B), the bf16 query with its weights (64 x 256 B + 64 x 4 B) and
+    the token's RoPE tables (2 x 32 x 4 B)."""
     tot = 0
     for b in range(wl.B):
         L = min(wl.T, int(inp.lens[b])) if inp.lens is not None else wl.T
         if wl.causal:
             L = min(L, wl.start_pos + 1)
         L = max(L, 0)
-        tot += max(L - 1, 0) * 132 + (256 + 132 if L >= 1 else 0) + wl.T * 4 + 64 * 128 * 2 + 64 * 4
+        tot += max(L - 1, 0) * 132 + (256 + 132 if L >= 1 else 0) + wl.T * 4 + 64 * 128 * 2 + 64 * 4 + 256
     return tot
 
 

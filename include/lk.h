@@ -44,6 +44,7 @@ extern "C" {
 #define LK_DIM 128          /* features per index head and per key (page "Index scores") */
 #define LK_HEADS 64         /* index heads (page "Index scores")                       */
 #define LK_TOPK_MAX_T 16384 /* longest score row lk_topk accepts (one row in LDS)      */
+#define LK_ROPE_DIM 64      /* leading features RoPE rotates (Indexer.forward excerpt)  */
 
 typedef enum lk_status {
     LK_OK = 0,
@@ -121,13 +122,25 @@ LK_API lk_status lk_quantize_queries(const uint16_t *q, const float *w, int64_t 
  * lk_quantize_keys and lk_quantize_queries in ONE kernel launch: the key write of
  * a step's new tokens and the query preparation are independent, and a decode step
  * is short enough that a second launch costs more than either job.  Arguments,
- * results and errors are exactly those of the two calls (either job may be empty).
+ * results and errors are those of the two calls (either job may be empty), plus
+ * optional RoPE (Indexer.forward excerpt: q_pe / k_pe rotated, "not interleaved",
+ * before rotate_activation; the NKI page takes cos / sin tables of rope_dim / 2
+ * entries per token): feature pairs (i, i + 32) of the leading LK_ROPE_DIM = 64
+ * features become
+ *   y_i = fl32(fl32(x_i c_i) - fl32(x_{i+32} s_i)),  y_{i+32} = fl32(fl32(x_i s_i) + fl32(x_{i+32} c_i)),
+ * each rounded to bf16 (nearest-even), before the Hadamard rotation.
+ *   k_rope_cos / k_rope_sin: float32 [n_seq * n_rows][32], one row per key row
+ *   (row b * n_rows + i), or both NULL for keys that need no rotation;
+ *   q_rope_cos / q_rope_sin: float32 [n_tokens][32], one row per query token (shared
+ *   by its heads), or both NULL.  Tables must be 16-byte aligned.
  */
 LK_API lk_status lk_prepare(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x_seq_stride,
                             uint8_t *cache, float *cache_scale, int64_t cache_seq_stride,
                             int64_t cache_rows, int64_t row_offset, const int32_t *positions,
                             const uint16_t *q, const float *w, int64_t n_tokens, int32_t heads,
-                            uint8_t *q_fp8, float *w_eff, float *q_scale, hipStream_t stream);
+                            uint8_t *q_fp8, float *w_eff, float *q_scale,
+                            const float *k_rope_cos, const float *k_rope_sin,
+                            const float *q_rope_cos, const float *q_rope_sin, hipStream_t stream);
 
 /*
  * fp8_index + mask (page "Index scores"): for every valid (b, t, s)
@@ -163,6 +176,8 @@ LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_
  *   scores [B, 1, T] float32, identical to lk_prepare + lk_index_score on the same inputs.
  *   q_fp8_out [B, heads, 128], w_eff_out [B, heads]: optional (both NULL or both set)
  *   copies of the quantized query and folded weights.
+ *   rope_cos / rope_sin: optional (both NULL or both set) float32 [B][32] tables of the
+ *   step's token, applied to the query heads and the new key as in lk_prepare.
  * Every block of the kernel quantizes its row's query while its key loads are in
  * flight, so the query preparation costs no separate launch.
  * Requires S == 1, heads == 64, T <= cache_seq_stride; q, k_new, k_cache and
@@ -171,7 +186,8 @@ LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_
 LK_API lk_status lk_decode_score(const uint16_t *q, const float *w, int32_t heads, const uint16_t *k_new,
                                  uint8_t *k_cache, float *k_scale, int64_t cache_seq_stride,
                                  const lk_rows *rows, float *scores, uint8_t *q_fp8_out,
-                                 float *w_eff_out, hipStream_t stream);
+                                 float *w_eff_out, const float *rope_cos, const float *rope_sin,
+                                 hipStream_t stream);
 
 /*
  * Per-row top-k of Indexer.forward (index_score.topk), with the NKI indexer's

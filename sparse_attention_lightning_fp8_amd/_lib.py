@@ -28,9 +28,10 @@ SIGNATURES = {
     "lk_quantize_keys": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _i64, _i64, _p, _p]),
     "lk_quantize_queries": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p, _p, _p]),
     "lk_prepare": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _i64, _i64, _p,
-                                  _p, _p, _i64, _i32, _p, _p, _p, _p]),
+                                  _p, _p, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _p]),
     "lk_index_score": (ctypes.c_int, [_p, _p, _i32, _p, _p, _i64, ctypes.POINTER(LkRows), _p, _p]),
-    "lk_decode_score": (ctypes.c_int, [_p, _p, _i32, _p, _p, _p, _i64, ctypes.POINTER(LkRows), _p, _p, _p, _p]),
+    "lk_decode_score": (ctypes.c_int, [_p, _p, _i32, _p, _p, _p, _i64, ctypes.POINTER(LkRows), _p, _p, _p,
+                                       _p, _p, _p]),
     "lk_topk": (ctypes.c_int, [_p, ctypes.POINTER(LkRows), _i32, _p, _p]),
     "lk_profile_next_launch": (ctypes.c_int, [_p, _p]),
     "lk_status_string": (ctypes.c_char_p, [ctypes.c_int]),

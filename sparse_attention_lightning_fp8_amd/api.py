@@ -17,6 +17,7 @@ from ._lib import LkRows
 
 DIM = 128
 HEADS = 64
+ROPE_DIM = 64
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -101,15 +102,31 @@ def lk_quantize_queries(q: torch.Tensor, w: torch.Tensor, q_fp8: Optional[torch.
     return q_fp8, w_eff
 
 
+def _rope_args(rope, n_rows: int, dev):
+    """(cos, sin) float32 [n_rows, 32] CUDA tables, or None -> two NULL pointers."""
+    if rope is None:
+        return None, None
+    c, s = rope
+    for t in (c, s):
+        _need(t.dtype == torch.float32 and t.is_cuda and t.device == dev and t.is_contiguous()
+              and t.numel() == n_rows * (ROPE_DIM // 2), f"RoPE tables must be contiguous float32 [{n_rows}, 32]")
+    return c.data_ptr(), s.data_ptr()
+
+
 def lk_prepare(x: torch.Tensor, cache: torch.Tensor, cache_scale: torch.Tensor, q: torch.Tensor,
                w: torch.Tensor, row_offset: int = 0, positions: Optional[torch.Tensor] = None,
                q_fp8: Optional[torch.Tensor] = None, w_eff: Optional[torch.Tensor] = None,
-               q_scale: Optional[torch.Tensor] = None):
-    """lk_quantize_keys + lk_quantize_queries in one kernel launch; returns (q_fp8, w_eff)."""
+               q_scale: Optional[torch.Tensor] = None, k_rope=None, q_rope=None):
+    """lk_quantize_keys + lk_quantize_queries in one kernel launch; returns (q_fp8, w_eff).
+    Optional RoPE before the rotation: k_rope = (cos, sin) float32 [n_seq * n_rows, 32]
+    (one row per key row), q_rope = (cos, sin) float32 [n_tokens, 32]."""
     kargs = _key_args(x, cache, cache_scale, row_offset, positions)
     qargs, q_fp8, w_eff = _query_args(q, w, q_fp8, w_eff, q_scale)
     _need(q.device == x.device, "tensors must be on one CUDA device")
-    _lib.check("lk_prepare", _lib.load().lk_prepare(*kargs, *qargs, _stream(x)))
+    kc, ks = _rope_args(k_rope, x.shape[0] * x.shape[1], x.device)
+    H = q.shape[-2]
+    qc, qs = _rope_args(q_rope, q.numel() // (H * DIM) if H > 0 else 0, x.device)
+    _lib.check("lk_prepare", _lib.load().lk_prepare(*kargs, *qargs, kc, ks, qc, qs, _stream(x)))
     return q_fp8, w_eff
 
 
@@ -144,11 +161,13 @@ def lk_index_score(q_fp8: torch.Tensor, w_eff: torch.Tensor, k_cache: torch.Tens
 def lk_decode_score(q: torch.Tensor, w: torch.Tensor, k_new: torch.Tensor, k_cache: torch.Tensor,
                     k_scale: torch.Tensor, T: int, start_pos: int = 0, seq_len: Optional[torch.Tensor] = None,
                     causal: bool = False, scores: Optional[torch.Tensor] = None,
-                    q_fp8_out: Optional[torch.Tensor] = None, w_eff_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    q_fp8_out: Optional[torch.Tensor] = None, w_eff_out: Optional[torch.Tensor] = None,
+                    rope=None) -> torch.Tensor:
     """One decode step up to the scores in one launch: writes k_new [B, 128] (bf16) to
     slot L-1 of each sequence's cache, quantizes q [B, 64, 128] (bf16) with weights
     w [B, 64] (float32), and returns masked scores [B, 1, T] (float32).  Optional
-    q_fp8_out [B, 64, 128] and w_eff_out [B, 64] receive the quantized query."""
+    q_fp8_out [B, 64, 128] and w_eff_out [B, 64] receive the quantized query; optional
+    rope = (cos, sin) float32 [B, 32] rotates the query and the new key first."""
     _need(q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[-1] == DIM, "q must be contiguous bf16 [B, H, 128]")
     H = q.shape[-2]
     B = q.numel() // (H * DIM) if H > 0 else 0
@@ -175,8 +194,9 @@ def lk_decode_score(q: torch.Tensor, w: torch.Tensor, k_new: torch.Tensor, k_cac
               "bad w_eff_out")
         q8p, wep = q8o.data_ptr(), w_eff_out.data_ptr()
     rows = _rows(B, 1, T, start_pos, seq_len, causal)
+    rc, rs = _rope_args(rope, B, q.device)
     st = _lib.load().lk_decode_score(q.data_ptr(), w.data_ptr(), H, k_new.data_ptr(), kc.data_ptr(), ks.data_ptr(),
-                                     seq_stride, ctypes.byref(rows), scores.data_ptr(), q8p, wep, _stream(q))
+                                     seq_stride, ctypes.byref(rows), scores.data_ptr(), q8p, wep, rc, rs, _stream(q))
     _lib.check("lk_decode_score", st)
     return scores
 

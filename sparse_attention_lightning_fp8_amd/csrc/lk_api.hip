@@ -12,7 +12,8 @@ hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const ui
 hipError_t launch_topk(const float *scores, const RowsDev &rows, int32_t k, int32_t *idx, hipStream_t stream);
 hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t *k_new, uint8_t *k_cache,
                                float *k_scale, int64_t cache_seq_stride, const RowsDev &rows, float *scores,
-                               uint8_t *q_fp8_out, float *w_eff_out, hipStream_t stream);
+                               uint8_t *q_fp8_out, float *w_eff_out, const float *rope_cos,
+                               const float *rope_sin, hipStream_t stream);
 }  // namespace lk
 
 namespace lk {
@@ -89,7 +90,14 @@ lk_status check_queries(const uint16_t *q, const float *w, int64_t n_tokens, int
     if (n_tokens > INT64_MAX / heads) return LK_E_UNSUPPORTED;
     const int64_t n_rows = n_tokens * heads;
     if ((n_rows + 31) / 32 > kMaxGridX / 2) return LK_E_UNSUPPORTED;
-    a = lk::QueryJobArgs{q, w, n_rows, q_fp8, w_eff, q_scale};
+    a = lk::QueryJobArgs{q, w, n_rows, q_fp8, w_eff, q_scale, heads};
+    return LK_OK;
+}
+
+// Optional RoPE tables: both or neither, 16-byte aligned.
+lk_status check_rope(const float *c, const float *s) {
+    if ((c == nullptr) != (s == nullptr)) return LK_E_NULL;
+    if (!aligned(c, 16) || !aligned(s, 16)) return LK_E_UNSUPPORTED;
     return LK_OK;
 }
 
@@ -127,7 +135,8 @@ LK_API lk_status lk_prepare(const uint16_t *x, int64_t n_seq, int64_t n_rows, in
                             uint8_t *cache, float *cache_scale, int64_t cache_seq_stride, int64_t cache_rows,
                             int64_t row_offset, const int32_t *positions, const uint16_t *q, const float *w,
                             int64_t n_tokens, int32_t heads, uint8_t *q_fp8, float *w_eff, float *q_scale,
-                            hipStream_t stream) {
+                            const float *k_rope_cos, const float *k_rope_sin, const float *q_rope_cos,
+                            const float *q_rope_sin, hipStream_t stream) {
     DisarmOnExit disarm;
     lk::KeyJobArgs ka;
     lk::QueryJobArgs qa;
@@ -136,6 +145,14 @@ LK_API lk_status lk_prepare(const uint16_t *x, int64_t n_seq, int64_t n_rows, in
     if (st != LK_OK) return st;
     st = check_queries(q, w, n_tokens, heads, q_fp8, w_eff, q_scale, qa);
     if (st != LK_OK) return st;
+    st = check_rope(k_rope_cos, k_rope_sin);
+    if (st != LK_OK) return st;
+    st = check_rope(q_rope_cos, q_rope_sin);
+    if (st != LK_OK) return st;
+    ka.rope_cos = k_rope_cos;
+    ka.rope_sin = k_rope_sin;
+    qa.rope_cos = q_rope_cos;
+    qa.rope_sin = q_rope_sin;
     return run_quantize(ka, qa, stream);
 }
 
@@ -161,9 +178,12 @@ LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_
 LK_API lk_status lk_decode_score(const uint16_t *q, const float *w, int32_t heads, const uint16_t *k_new,
                                  uint8_t *k_cache, float *k_scale, int64_t cache_seq_stride,
                                  const lk_rows *rows, float *scores, uint8_t *q_fp8_out,
-                                 float *w_eff_out, hipStream_t stream) {
+                                 float *w_eff_out, const float *rope_cos, const float *rope_sin,
+                                 hipStream_t stream) {
     DisarmOnExit disarm;
     lk_status st = check_rows(rows);
+    if (st != LK_OK) return st;
+    st = check_rope(rope_cos, rope_sin);
     if (st != LK_OK) return st;
     if (cache_seq_stride < 0 || rows->T > cache_seq_stride) return LK_E_SHAPE;
     if (rows->S > 1) return LK_E_SHAPE;
@@ -177,7 +197,7 @@ LK_API lk_status lk_decode_score(const uint16_t *q, const float *w, int32_t head
         return LK_E_UNSUPPORTED;
     if (rows->B > kMaxGridYZ || rows->T > kMaxGridX) return LK_E_UNSUPPORTED;
     return from_hip(lk::launch_decode_score(q, w, k_new, k_cache, k_scale, cache_seq_stride, to_dev(*rows), scores,
-                                            q_fp8_out, w_eff_out, stream));
+                                            q_fp8_out, w_eff_out, rope_cos, rope_sin, stream));
 }
 
 LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, int32_t *idx, hipStream_t stream) {

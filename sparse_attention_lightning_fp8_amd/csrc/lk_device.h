@@ -71,6 +71,7 @@ struct KeyJobArgs {
     float *cache_scale = nullptr;
     int64_t cache_seq_stride = 0, cache_rows = 0, row_offset = 0;
     const int32_t *positions = nullptr;
+    const float *rope_cos = nullptr, *rope_sin = nullptr;   // optional [n_seq * n_rows][32]
 };
 struct QueryJobArgs {
     const uint16_t *q = nullptr;
@@ -78,6 +79,8 @@ struct QueryJobArgs {
     int64_t n_rows = 0;
     uint8_t *q_fp8 = nullptr;
     float *w_eff = nullptr, *q_scale = nullptr;
+    int32_t heads = 0;                                      // rows per token (for the RoPE tables)
+    const float *rope_cos = nullptr, *rope_sin = nullptr;   // optional [n_rows / heads][32]
 };
 
 // Events armed by lk_profile_next_launch for the calling thread's next launch.

@@ -114,6 +114,94 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
     }
 }
 
+// Round a finite float to bf16 bits, nearest-even.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// RoPE of Indexer.forward on the leading 64 features of the row owned by this 8-lane
+// group ("rope in indexer is not interleaved": feature i pairs with i + 32).  `in`
+// holds the lane's 16 bf16 features 16 * sub .. 16 * sub + 15 (two per dword); the
+// partner features of lanes 0 and 1 live in lanes 2 and 3.  Products and sums are
+// rounded in fp32 (no fused multiply-add), then each result once to bf16.  Lanes 4-7
+// keep their features.
+
+// This lane's 16 cosines and sines (pairs 16 * (sub % 2) + e) of one token's table
+// row.  Every lane loads (lanes 4-7 read the same rows and ignore them), so callers
+// can issue these loads ahead of others without a branch.
+struct Rope16 {
+    float c[16], s[16];
+};
+__device__ __forceinline__ void load_rope16(const float *__restrict__ cos_row, const float *__restrict__ sin_row,
+                                            int sub, Rope16 &r) {
+    const float4 *c4 = reinterpret_cast<const float4 *>(cos_row + 16 * (sub & 1));
+    const float4 *s4 = reinterpret_cast<const float4 *>(sin_row + 16 * (sub & 1));
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float4 cv = c4[q], sv = s4[q];
+        r.c[4 * q] = cv.x; r.c[4 * q + 1] = cv.y; r.c[4 * q + 2] = cv.z; r.c[4 * q + 3] = cv.w;
+        r.s[4 * q] = sv.x; r.s[4 * q + 1] = sv.y; r.s[4 * q + 2] = sv.z; r.s[4 * q + 3] = sv.w;
+    }
+}
+
+// A whole table row (32 cosines, 32 sines) read through a block-uniform address, so
+// the loads go through the scalar path and each lane picks its 16 with pick_rope16.
+struct Rope32 {
+    float c[32], s[32];
+};
+typedef const float __attribute__((address_space(4))) *const_f32_ptr;
+__device__ __forceinline__ void load_rope32_uniform(const float *__restrict__ cos_row,
+                                                    const float *__restrict__ sin_row, Rope32 &r) {
+    // The tables are read-only for the kernel's lifetime, so the constant address
+    // space is valid for them; with a uniform address that makes them scalar loads.
+    const const_f32_ptr c = (const_f32_ptr)(uintptr_t)cos_row;
+    const const_f32_ptr sn = (const_f32_ptr)(uintptr_t)sin_row;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+        r.c[i] = c[i];
+        r.s[i] = sn[i];
+    }
+}
+__device__ __forceinline__ void pick_rope16(const Rope32 &all, int sub, Rope16 &r) {
+    const bool hi = (sub & 1) != 0;
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+        r.c[e] = hi ? all.c[16 + e] : all.c[e];
+        r.s[e] = hi ? all.s[16 + e] : all.s[e];
+    }
+}
+
+// Every lane of the group must call it (it exchanges registers with lane sub ^ 2).
+__device__ __forceinline__ void rope_row16(uint32_t in[8], const Rope16 &r, int sub) {
+#pragma clang fp contract(off)
+    uint32_t partner[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) partner[i] = (uint32_t)__shfl_xor((int)in[i], 2, 64);
+    if (sub >= 4) return;
+    const bool first = sub < 2;                        // this lane holds x_i (else x_{i+32})
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        uint32_t outw = 0;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int e = 2 * i + h;
+            const float own = __uint_as_float(((in[i] >> (16 * h)) & 0xFFFFu) << 16);
+            const float oth = __uint_as_float(((partner[i] >> (16 * h)) & 0xFFFFu) << 16);
+            float y;
+            if (first) {
+                const float ac = own * r.c[e], bs = oth * r.s[e];
+                y = ac - bs;
+            } else {
+                const float as = oth * r.s[e], bc = own * r.c[e];
+                y = as + bc;
+            }
+            outw |= f32_to_bf16_bits(y) << (16 * h);
+        }
+        in[i] = outw;
+    }
+}
+
 // Folded query weight of page "Index scores": fl32(fl32(w * 2^j) * fl32(128^-0.5)).
 __device__ __forceinline__ float fold_weight(float w, int j) {
     const float ws = __fmul_rn(w, __builtin_ldexpf(1.0f, j));   // exact unless it leaves the float range

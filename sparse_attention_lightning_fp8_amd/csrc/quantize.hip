@@ -25,6 +25,7 @@ struct KeyJob {
     float *cache_scale;
     int64_t cache_seq_stride, cache_rows, row_offset;
     const int32_t *positions;
+    const float *rope_cos, *rope_sin;
 };
 
 struct QueryJob {
@@ -33,6 +34,8 @@ struct QueryJob {
     int64_t n_rows;
     uint8_t *q_fp8;
     float *w_eff, *q_scale;
+    int64_t heads;
+    const float *rope_cos, *rope_sin;
 };
 
 // Row g of the key job, owned by the 8 lanes of this row group (sub = lane in group).
@@ -42,6 +45,11 @@ __device__ __forceinline__ void key_row(const KeyJob &k, int64_t g, int sub) {
     const uint4 *src = reinterpret_cast<const uint4 *>(k.x + (b * k.x_seq_stride + i) * LK_DIM + sub * 16);
     uint4 v0 = src[0], v1 = src[1];
     uint32_t in[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    if (k.rope_cos) {
+        Rope16 r;
+        load_rope16(k.rope_cos + g * (LK_ROPE_DIM / 2), k.rope_sin + g * (LK_ROPE_DIM / 2), sub, r);
+        rope_row16(in, r, sub);
+    }
     uint32_t out[4];
     int j;
     quantize_row16(in, out, j);
@@ -56,6 +64,12 @@ __device__ __forceinline__ void query_row(const QueryJob &q, int64_t g, int sub)
     const uint4 *src = reinterpret_cast<const uint4 *>(q.q + g * LK_DIM + sub * 16);
     uint4 v0 = src[0], v1 = src[1];
     uint32_t in[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    if (q.rope_cos) {
+        const int64_t tok = g / q.heads;
+        Rope16 r;
+        load_rope16(q.rope_cos + tok * (LK_ROPE_DIM / 2), q.rope_sin + tok * (LK_ROPE_DIM / 2), sub, r);
+        rope_row16(in, r, sub);
+    }
     uint32_t out[4];
     int j;
     quantize_row16(in, out, j);
@@ -86,8 +100,9 @@ quantize_kernel(KeyJob kj, QueryJob qj, int64_t key_blocks) {
 // Either job may be empty (n rows == 0); one launch covers both.
 hipError_t launch_quantize(const KeyJobArgs &ka, const QueryJobArgs &qa, hipStream_t stream) {
     KeyJob kj{ka.x, ka.n_seq, ka.n_rows, ka.x_seq_stride, ka.cache, ka.cache_scale, ka.cache_seq_stride,
-              ka.cache_rows, ka.row_offset, ka.positions};
-    QueryJob qj{qa.q, qa.w, qa.n_rows, qa.q_fp8, qa.w_eff, qa.q_scale};
+              ka.cache_rows, ka.row_offset, ka.positions, ka.rope_cos, ka.rope_sin};
+    QueryJob qj{qa.q, qa.w, qa.n_rows, qa.q_fp8, qa.w_eff, qa.q_scale, qa.heads > 0 ? qa.heads : 1,
+                qa.rope_cos, qa.rope_sin};
     const int64_t key_blocks = (ka.n_seq * ka.n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
     const int64_t query_blocks = (qa.n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
     return launch(quantize_kernel, dim3((unsigned)(key_blocks + query_blocks)), dim3(256), 0u, stream, kj, qj,

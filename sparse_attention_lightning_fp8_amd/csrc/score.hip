@@ -137,6 +137,8 @@ struct DecodeArgs {
     const uint16_t *k_new;      // [B, 128] bf16 new keys     (fused)
     uint8_t *q_fp8_out;         // optional copies of the quantized query (fused)
     float *w_eff_out;
+    const float *rope_cos;      // optional [B][32] RoPE tables of the step's token (fused)
+    const float *rope_sin;
     uint8_t *k_cache;           // [B, stride, 128]; the fused kernel writes row L-1
     float *k_scale;             // [B, stride]
     int64_t cache_seq_stride;
@@ -169,6 +171,11 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
                 const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
                 const uint4 q0 = qs[0], q1 = qs[1];
                 uint32_t in[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                if (a.rope_cos) {
+                    Rope16 rr;
+                    load_rope16(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2), a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), sub, rr);
+                    rope_row16(in, rr, sub);
+                }
                 uint32_t codes[4];
                 int j;
                 quantize_row16(in, codes, j);
@@ -188,6 +195,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
     uint4 qp0, qp1, kn0, kn1;
     float4 wv;
     float wr = 0.f;
+    Rope32 rope_row;                                   // fused: the token's RoPE table row (scalar loads)
     if constexpr (kFused) {
         const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
         qp0 = qs[0];
@@ -196,6 +204,9 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
         const uint4 *kns = reinterpret_cast<const uint4 *>(a.k_new + (int64_t)b * LK_DIM + 16 * sub);
         kn0 = kns[0];
         kn1 = kns[1];
+        if (a.rope_cos)                                // the step's token: shared by the query and the new key
+            load_rope32_uniform(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2),
+                                a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), rope_row);
     } else {
         qp0 = reinterpret_cast<const uint4 *>(a.q_fp8 + (int64_t)qrow * LK_HEADS * LK_DIM)[threadIdx.x];
         // Every thread loads and stores a float4 of the weights (lane % 16 picks which).
@@ -223,6 +234,11 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kFused) {
         uint32_t in[8] = {qp0.x, qp0.y, qp0.z, qp0.w, qp1.x, qp1.y, qp1.z, qp1.w};
+        Rope16 rope;
+        if (a.rope_cos) {
+            pick_rope16(rope_row, sub, rope);
+            rope_row16(in, rope, sub);
+        }
         uint32_t codes[4];
         int j;
         quantize_row16(in, codes, j);
@@ -236,6 +252,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
         }
         if (has_new && wave == 0) {                    // all 8 row groups of wave 0 compute the same key
             uint32_t kin[8] = {kn0.x, kn0.y, kn0.z, kn0.w, kn1.x, kn1.y, kn1.z, kn1.w};
+            if (a.rope_cos) rope_row16(kin, rope, sub);
             uint32_t kc[4];
             int kj;
             quantize_row16(kin, kc, kj);
@@ -493,8 +510,11 @@ hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const ui
 // done inside the score kernel.
 hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t *k_new, uint8_t *k_cache,
                                float *k_scale, int64_t cache_seq_stride, const RowsDev &rows, float *scores,
-                               uint8_t *q_fp8_out, float *w_eff_out, hipStream_t stream) {
+                               uint8_t *q_fp8_out, float *w_eff_out, const float *rope_cos,
+                               const float *rope_sin, hipStream_t stream) {
     DecodeArgs a{};
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
     a.q_bf16 = q;
     a.w = w;
     a.k_new = k_new;

@@ -105,6 +105,26 @@ def make_inputs(wl: Workload, seed: int = 0) -> Inputs:
     return Inputs(wl, q, k, w, lens, positions)
 
 
+ROPE_DIM = 64
+ROPE_THETA = 10000.0
+
+
+def rope_tables(positions):
+    """cos / sin float32 [n, ROPE_DIM / 2] of plain RoPE angles pos * THETA^(-2i/ROPE_DIM)
+    for the given absolute positions (angles in float64, then rounded to float32)."""
+    import numpy as np
+    inv = ROPE_THETA ** (-np.arange(ROPE_DIM // 2, dtype=np.float64) * 2.0 / ROPE_DIM)
+    ang = np.asarray(positions, np.float64).reshape(-1, 1) * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def query_positions(inp: "Inputs"):
+    """Absolute position of every query token, [B, S] int64 (token t of sequence b sits
+    at positions[b] + t)."""
+    import numpy as np
+    return inp.positions.numpy().astype(np.int64)[:, None] + np.arange(inp.wl.S, dtype=np.int64)[None, :]
+
+
 def bf16_bits(t: torch.Tensor):
     """numpy uint16 view of a bfloat16 CPU tensor's bit patterns."""
     import numpy as np

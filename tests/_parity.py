@@ -35,11 +35,14 @@ class OracleRow:
 
 
 class OracleCase:
-    """Oracle results for selected query rows of a workload."""
+    """Oracle results for selected query rows of a workload.  With `rope`, every key and
+    query row is rotated by RoPE at its absolute position first (key: its cache row;
+    query token t of sequence b: positions[b] + t)."""
 
-    def __init__(self, inp: W.Inputs):
+    def __init__(self, inp: W.Inputs, rope: bool = False):
         self.inp = inp
         self.wl = inp.wl
+        self.rope = rope
         self._kq: Dict[int, tuple] = {}
 
     def keys(self, b: int, n: int):
@@ -47,14 +50,22 @@ class OracleCase:
         got = self._kq.get(b)
         if got is None or got[0].shape[0] < n:
             bits = W.bf16_bits(self.inp.k[b, :n])
-            codes, scales = O.quantize_rows(bits)
+            if self.rope:
+                c, s = W.rope_tables(np.arange(n))
+                codes, scales = O.rope_quantize_rows(bits, c, s)
+            else:
+                codes, scales = O.quantize_rows(bits)
             self._kq[b] = (codes, scales)
         codes, scales = self._kq[b]
         return codes[:n], scales[:n]
 
     def query(self, b: int, t: int):
         bits = W.bf16_bits(self.inp.q[b, t])
-        q8, qs = O.quantize_rows(bits)
+        if self.rope:
+            c, s = W.rope_tables([W.query_positions(self.inp)[b, t]])
+            q8, qs = O.rope_quantize_rows(bits, c, s, rows_per_table_row=64)
+        else:
+            q8, qs = O.quantize_rows(bits)
         w_eff = O.fold_weights(self.inp.w[b, t].numpy(), qs)
         return q8, qs, w_eff
 
@@ -88,10 +99,35 @@ class GpuResult:
     idx: torch.Tensor
 
 
-def gpu_pipeline(inp: W.Inputs, device="cuda:0", new_rows_only: bool = False) -> GpuResult:
+def _rope_dev(positions, device):
+    c, s = W.rope_tables(positions)
+    return torch.from_numpy(c).to(device), torch.from_numpy(s).to(device)
+
+
+def write_prefix(inp: W.Inputs, cache, cache_scale, rope: bool, device="cuda:0", upto=None) -> None:
+    """Write cache rows [0, upto[b]) of every sequence (all rows if upto is None),
+    rotated by RoPE at their positions when `rope` is set."""
+    from sparse_attention_lightning_fp8_amd import api
+    wl = inp.wl
+    k = inp.k.to(device)
+    if upto is None and not rope:
+        api.lk_quantize_keys(k, cache, cache_scale, row_offset=0)
+        return
+    q0 = torch.empty((0, 64, 128), dtype=torch.bfloat16, device=device)
+    w0 = torch.empty((0, 64), dtype=torch.float32, device=device)
+    for b in range(wl.B):
+        n = wl.cap if upto is None else int(upto[b])
+        if n <= 0:
+            continue
+        api.lk_prepare(k[b:b + 1, :n], cache[b:b + 1], cache_scale[b:b + 1], q0, w0,
+                       k_rope=_rope_dev(np.arange(n), device) if rope else None)
+
+
+def gpu_pipeline(inp: W.Inputs, device="cuda:0", rope: bool = False) -> GpuResult:
     """The hot path through the C ABI: cache prefix written first, then one step:
     key write of the step's rows with query quantize + fold (one lk_prepare launch),
-    index score, top-k."""
+    index score, top-k.  With `rope`, keys and queries are rotated by RoPE at their
+    positions."""
     from sparse_attention_lightning_fp8_amd import api
     wl = inp.wl
     k = inp.k.to(device)
@@ -99,7 +135,7 @@ def gpu_pipeline(inp: W.Inputs, device="cuda:0", new_rows_only: bool = False) ->
     cache_scale = torch.zeros((wl.B, wl.cap), dtype=torch.float32, device=device)
     positions = inp.positions.to(device)
     # prefix: every cache row, then the step's own rows again through `positions`
-    api.lk_quantize_keys(k, cache, cache_scale, row_offset=0)
+    write_prefix(inp, cache, cache_scale, rope, device)
     rows_step = k.new_empty((wl.B, wl.S, 128))
     for b in range(wl.B):
         p0 = int(inp.positions[b])
@@ -107,7 +143,11 @@ def gpu_pipeline(inp: W.Inputs, device="cuda:0", new_rows_only: bool = False) ->
     q = inp.q.to(device)
     w = inp.w.to(device)
     q_scale = torch.empty_like(w)
-    q_fp8, w_eff = api.lk_prepare(rows_step, cache, cache_scale, q, w, positions=positions, q_scale=q_scale)
+    qpos = W.query_positions(inp)
+    k_rope = _rope_dev(qpos.reshape(-1), device) if rope else None     # the step's keys sit at the query positions
+    q_rope = _rope_dev(qpos.reshape(-1), device) if rope else None
+    q_fp8, w_eff = api.lk_prepare(rows_step, cache, cache_scale, q, w, positions=positions, q_scale=q_scale,
+                                  k_rope=k_rope, q_rope=q_rope)
     seq_len = inp.lens.to(device) if inp.lens is not None else None
     scores = api.lk_index_score(q_fp8, w_eff, cache, cache_scale, wl.T, start_pos=wl.start_pos,
                                 seq_len=seq_len, causal=wl.causal)
@@ -116,11 +156,12 @@ def gpu_pipeline(inp: W.Inputs, device="cuda:0", new_rows_only: bool = False) ->
     return GpuResult(cache, cache_scale, q_fp8, w_eff, q_scale, scores, idx)
 
 
-def gpu_pipeline_fused(inp: W.Inputs, device="cuda:0") -> GpuResult:
+def gpu_pipeline_fused(inp: W.Inputs, device="cuda:0", rope: bool = False) -> GpuResult:
     """The fused decode step through the C ABI: the cache prefix [0, L-1) of each
     sequence is written first (slot L-1 and beyond hold 0xAA garbage), then one
     lk_decode_score launch writes the new key at L-1, quantizes the query and scores,
-    then lk_topk."""
+    then lk_topk.  With `rope`, the prefix keys are rotated at their positions and the
+    step's query and new key at position L-1."""
     from sparse_attention_lightning_fp8_amd import api
     wl = inp.wl
     assert wl.S == 1
@@ -129,18 +170,22 @@ def gpu_pipeline_fused(inp: W.Inputs, device="cuda:0") -> GpuResult:
     cache_scale = torch.full((wl.B, wl.cap), 3.0, dtype=torch.float32, device=device)
     seq_len = inp.lens.to(device) if inp.lens is not None else None
     new_rows = k.new_empty((wl.B, 128))
+    Ls = []
     for b in range(wl.B):
         sl = int(inp.lens[b]) if inp.lens is not None else -1
         L = O.valid_len(wl.T, sl, wl.causal, wl.start_pos, 0)
-        if L > 1:
-            api.lk_quantize_keys(k[b:b + 1, :L - 1], cache[b:b + 1], cache_scale[b:b + 1])
+        Ls.append(L)
         new_rows[b] = k[b, max(L - 1, 0)]
+    write_prefix(inp, cache, cache_scale, rope, device, upto=[max(L - 1, 0) for L in Ls])
+    # the step's token sits at positions[b] (= L - 1 whenever L >= 1): its table row
+    # rotates both the query and the new key
+    rope_t = _rope_dev(W.query_positions(inp)[:, 0], device) if rope else None
     q = inp.q.to(device).reshape(wl.B, 64, 128)
     w = inp.w.to(device).reshape(wl.B, 64)
     q_fp8 = torch.empty((wl.B, 1, 64, 128), dtype=torch.uint8, device=device)
     w_eff = torch.empty((wl.B, 1, 64), dtype=torch.float32, device=device)
     scores = api.lk_decode_score(q, w, new_rows, cache, cache_scale, wl.T, start_pos=wl.start_pos,
-                                 seq_len=seq_len, causal=wl.causal, q_fp8_out=q_fp8, w_eff_out=w_eff)
+                                 seq_len=seq_len, causal=wl.causal, q_fp8_out=q_fp8, w_eff_out=w_eff, rope=rope_t)
     idx = api.lk_topk(scores, wl.k, start_pos=wl.start_pos, seq_len=seq_len, causal=wl.causal)
     torch.cuda.synchronize()
     return GpuResult(cache, cache_scale, q_fp8, w_eff, None, scores, idx)

@@ -79,12 +79,16 @@ def test_prepare_validation(lib):
     f = lib.lk_prepare
     K = (A, 1, 1, 1, A, A, 16, 16, 0, None)
     Q = (A, A, 1, 64, A, A, None)
-    assert f(A, -1, 1, 1, A, A, 16, 16, 0, None, *Q, None) == E_SHAPE
-    assert f(*K, A, A, -1, 64, A, A, None, None) == E_SHAPE
-    assert f(*K, None, A, 1, 64, A, A, None, None) == E_NULL
-    assert f(None, 1, 1, 1, A, A, 16, 16, 0, None, *Q, None) == E_NULL
-    assert f(*K, A + 4, A, 1, 64, A, A, None, None) == E_UNSUP
-    assert f(None, 0, 0, 0, None, None, 0, 0, 0, None, None, None, 0, 64, None, None, None, None) == OK
+    R = (None, None, None, None)
+    assert f(A, -1, 1, 1, A, A, 16, 16, 0, None, *Q, *R, None) == E_SHAPE
+    assert f(*K, A, A, -1, 64, A, A, None, *R, None) == E_SHAPE
+    assert f(*K, None, A, 1, 64, A, A, None, *R, None) == E_NULL
+    assert f(None, 1, 1, 1, A, A, 16, 16, 0, None, *Q, *R, None) == E_NULL
+    assert f(*K, A + 4, A, 1, 64, A, A, None, *R, None) == E_UNSUP
+    assert f(*K, *Q, A, None, None, None, None) == E_NULL                  # RoPE tables come in pairs
+    assert f(*K, *Q, None, None, None, A, None) == E_NULL
+    assert f(*K, *Q, A + 4, A, None, None, None) == E_UNSUP                # misaligned table
+    assert f(None, 0, 0, 0, None, None, 0, 0, 0, None, None, None, 0, 64, None, None, None, *R, None) == OK
 
 
 def test_index_score_validation(lib):
@@ -106,21 +110,23 @@ def test_index_score_validation(lib):
 
 def test_decode_score_validation(lib):
     f = lib.lk_decode_score
-    #       q  w   H   kn k_cache k_scale stride rows      scores q8o  weo  stream
-    assert f(A, A, 64, A, A, A, 16, None, A, None, None, None) == E_NULL
-    assert f(A, A, 64, A, A, A, 16, rows(S=2), A, None, None, None) == E_SHAPE      # decode rows only
-    assert f(A, A, 64, A, A, A, 16, rows(T=17), A, None, None, None) == E_SHAPE     # T beyond the cache
-    assert f(A, A, 32, A, A, A, 16, rows(), A, None, None, None) == E_UNSUP         # heads != 64
-    assert f(A, A, 64, A, A, A, 16, rows(), A, A, None, None) == E_NULL             # one optional output
-    assert f(None, A, 64, A, A, A, 16, rows(), A, None, None, None) == E_NULL
-    assert f(A, A, 64, None, A, A, 16, rows(), A, None, None, None) == E_NULL
-    assert f(A, A, 64, A, A, A, 16, rows(), None, None, None, None) == E_NULL
-    assert f(A + 8, A, 64, A, A, A, 16, rows(), A, None, None, None) == E_UNSUP     # misaligned q
-    assert f(A, A, 64, A + 8, A, A, 16, rows(), A, None, None, None) == E_UNSUP     # misaligned k_new
-    assert f(A, A + 2, 64, A, A, A, 16, rows(), A, None, None, None) == E_UNSUP
-    assert f(A, A, 64, A, A, A, 16, rows(), A, A + 4, A, None) == E_UNSUP
-    assert f(A, A, 64, A, A, A, 70000, rows(B=70000, T=16), A, None, None, None) == E_UNSUP
-    assert f(None, None, 64, None, None, None, 16, rows(B=0), None, None, None, None) == OK
+    #       q  w   H   kn k_cache k_scale stride rows      scores q8o  weo  cos sin stream
+    assert f(A, A, 64, A, A, A, 16, None, A, None, None, None, None, None) == E_NULL
+    assert f(A, A, 64, A, A, A, 16, rows(S=2), A, None, None, None, None, None) == E_SHAPE      # decode rows only
+    assert f(A, A, 64, A, A, A, 16, rows(T=17), A, None, None, None, None, None) == E_SHAPE     # T beyond the cache
+    assert f(A, A, 32, A, A, A, 16, rows(), A, None, None, None, None, None) == E_UNSUP         # heads != 64
+    assert f(A, A, 64, A, A, A, 16, rows(), A, A, None, None, None, None) == E_NULL             # one optional output
+    assert f(None, A, 64, A, A, A, 16, rows(), A, None, None, None, None, None) == E_NULL
+    assert f(A, A, 64, None, A, A, 16, rows(), A, None, None, None, None, None) == E_NULL
+    assert f(A, A, 64, A, A, A, 16, rows(), None, None, None, None, None, None) == E_NULL
+    assert f(A + 8, A, 64, A, A, A, 16, rows(), A, None, None, None, None, None) == E_UNSUP     # misaligned q
+    assert f(A, A, 64, A + 8, A, A, 16, rows(), A, None, None, None, None, None) == E_UNSUP     # misaligned k_new
+    assert f(A, A + 2, 64, A, A, A, 16, rows(), A, None, None, None, None, None) == E_UNSUP
+    assert f(A, A, 64, A, A, A, 16, rows(), A, A + 4, A, None, None, None) == E_UNSUP
+    assert f(A, A, 64, A, A, A, 70000, rows(B=70000, T=16), A, None, None, None, None, None) == E_UNSUP
+    assert f(A, A, 64, A, A, A, 16, rows(), A, None, None, A, None, None) == E_NULL     # RoPE pair
+    assert f(A, A, 64, A, A, A, 16, rows(), A, None, None, A + 8, A, None) == E_UNSUP
+    assert f(None, None, 64, None, None, None, 16, rows(B=0), None, None, None, None, None, None) == OK
 
 
 def test_topk_validation(lib):
