@@ -46,6 +46,14 @@
  *      each then rounded to bf16 (nearest-even); features >= rope_dim are unchanged.
  *      rope_dim is 64 for the indexer's 128-feature heads.
  *
+ *   R13 sparse MLA decode (page "Join query parts", MQA-decode excerpt): for one
+ *      decode row and head h, s_t = scale * (qc_h . c_t + qr_h . r_t) over the selected
+ *      set I only (the index mask is -inf elsewhere), p = softmax over I,
+ *      o_h = sum_{t in I} p_t c_t (the 512-wide latent; the output projection is out of
+ *      scope).  Queries, latent cache c and rotary cache r are bf16; the oracle works
+ *      in fp64.  Entries -1 of the index list are unused slots; the others are
+ *      distinct.  A row whose index list is empty returns zeros.
+ *
  * Parity with DeepSeek's own act_quant / fp8_index bytes is unpinned: the pages print
  * no numbers, so R1-R5 cannot be checked against the reference's outputs.
  *
@@ -439,4 +447,49 @@ int lko_topk_f32(const float *v, int64_t L, int k, int32_t *out)
     rc = topk_sorted(items, L, k, out);
     free(items);
     return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Sparse MLA decode attention over the selected indices (reading R13).       */
+/* ------------------------------------------------------------------------- */
+/* qc [H][Dc], qr [H][Dr] bf16; kv [T][Dc], pe [T][Dr] bf16 (one sequence); idx [n_idx]
+ * int32 (-1 = unused); out [H][Dc] fp64.  Returns LKO_E_ARG for an index outside
+ * [0, T). */
+int lko_sparse_mla_row(const uint16_t *qc, const uint16_t *qr, int H, int Dc, int Dr,
+                       const uint16_t *kv, const uint16_t *pe, int64_t T, const int32_t *idx,
+                       int n_idx, double scale, double *out)
+{
+    for (int i = 0; i < n_idx; i++)
+        if (idx[i] >= T || idx[i] < -1) return LKO_E_ARG;
+    double *s = (double *)malloc(sizeof(double) * (n_idx > 0 ? n_idx : 1));
+    if (!s) return LKO_E_ARG;
+    for (int h = 0; h < H; h++) {
+        double *o = out + (int64_t)h * Dc;
+        for (int c = 0; c < Dc; c++) o[c] = 0.0;
+        double m = -INFINITY;
+        int any = 0;
+        for (int i = 0; i < n_idx; i++) {
+            if (idx[i] < 0) continue;
+            const uint16_t *kt = kv + (int64_t)idx[i] * Dc;
+            const uint16_t *rt = pe + (int64_t)idx[i] * Dr;
+            double dot = 0.0;
+            for (int c = 0; c < Dc; c++) dot += lko_bf16_decode(qc[(int64_t)h * Dc + c]) * lko_bf16_decode(kt[c]);
+            for (int c = 0; c < Dr; c++) dot += lko_bf16_decode(qr[(int64_t)h * Dr + c]) * lko_bf16_decode(rt[c]);
+            s[i] = scale * dot;
+            if (s[i] > m) m = s[i];
+            any = 1;
+        }
+        if (!any) continue;
+        double l = 0.0;
+        for (int i = 0; i < n_idx; i++) {
+            if (idx[i] < 0) continue;
+            const double p = exp(s[i] - m);
+            l += p;
+            const uint16_t *kt = kv + (int64_t)idx[i] * Dc;
+            for (int c = 0; c < Dc; c++) o[c] += p * lko_bf16_decode(kt[c]);
+        }
+        for (int c = 0; c < Dc; c++) o[c] /= l;
+    }
+    free(s);
+    return LKO_OK;
 }

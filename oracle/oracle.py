@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.lko_quantize_rows.argtypes = [p, i64, ctypes.c_int, p, p]
         L.lko_fold_weights.argtypes = [p, p, i64, ctypes.c_int, p]
         L.lko_rope_row.argtypes = [p, ctypes.c_int, ctypes.c_int, p, p, p]
+        L.lko_sparse_mla_row.argtypes = [p, p, ctypes.c_int, ctypes.c_int, ctypes.c_int, p, p, i64, p,
+                                         ctypes.c_int, ctypes.c_double, p]
         L.lko_rope_quantize_rows.argtypes = [p, i64, ctypes.c_int, ctypes.c_int, p, p, i64, p, p]
         L.lko_fold_weights.restype = None
         L.lko_valid_len.argtypes = [i64, i64, ctypes.c_int, i64, i64]
@@ -208,4 +210,23 @@ def topk(values: np.ndarray, L: int, k: int) -> np.ndarray:
         v = np.ascontiguousarray(v, dtype=np.float64)
         rc = lib().lko_topk_f64(_ptr(v), L, k, _ptr(out))
     _check(rc, "topk")
+    return out
+
+
+def sparse_mla_row(qc_bits: np.ndarray, qr_bits: np.ndarray, kv_bits: np.ndarray, pe_bits: np.ndarray,
+                   idx: np.ndarray, scale: float) -> np.ndarray:
+    """Sparse MLA decode attention of one row (reading R13): qc [H, Dc], qr [H, Dr] bf16
+    bits, kv [T, Dc], pe [T, Dr] bf16 bits, idx int32 (-1 unused) -> float64 [H, Dc]."""
+    qc = np.ascontiguousarray(qc_bits, np.uint16)
+    qr = np.ascontiguousarray(qr_bits, np.uint16)
+    kv = np.ascontiguousarray(kv_bits, np.uint16)
+    pe = np.ascontiguousarray(pe_bits, np.uint16)
+    ix = np.ascontiguousarray(idx, np.int32)
+    H, Dc = qc.shape
+    Dr = qr.shape[1]
+    T = kv.shape[0]
+    assert pe.shape == (T, Dr) and kv.shape[1] == Dc
+    out = np.empty((H, Dc), np.float64)
+    _check(lib().lko_sparse_mla_row(_ptr(qc), _ptr(qr), H, Dc, Dr, _ptr(kv), _ptr(pe), T, _ptr(ix), ix.size,
+                                    float(scale), _ptr(out)), "sparse_mla_row")
     return out
