@@ -12,8 +12,9 @@ the inputs are rotated so the 256 MB last-level cache cannot serve the 33 MB key
 cache.  The same step through the separate entry points (lk_prepare, lk_index_score,
 lk_topk) is timed too and reported under "extra".
 
-Prints ONE JSON line.  Prefill (4096x4096 causal) and chunked prefill (2 x 4096 new
-tokens against 16384 keys) are timed too and reported under "extra".
+Prints ONE JSON line.  Prefill (4096x4096 causal), chunked prefill (2 x 4096 new
+tokens against 16384 keys) and the sparse MLA decode attention over the selected
+slots (16 rows, 2048 of 16384) are timed too and reported under "extra".
 """
 from __future__ import annotations
 
@@ -31,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "decode keys scored/s + HBM GB/s (B16,T16K); prefill index fp8 TFLOP/s"
 HBM_PEAK_GBPS = 8000.0
 F16_PEAK_TFLOPS = 2500.0      # dense f16 MFMA (the dtype the contraction runs in)
+BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0      # dense fp8 MFMA
 BYTES_PER_KEY = 136           # 128 B key + 4 B key scale + 4 B score
 BYTES_PER_QUERY_ROW = 64 * (128 + 4)
@@ -52,6 +54,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=16, help="input copies cycled through to defeat the LLC")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-mla", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
@@ -222,6 +225,63 @@ def valid_pairs(wl, inp):
     return tot
 
 
+def time_mla(api, steps, warmup, n_sets, dev):
+    """Sparse MLA decode over the 2048 selected slots of 16 rows (16384-slot latent
+    cache).  n_sets copies of the caches and index lists (seeded, generated on the GPU)
+    are rotated so the last-level cache cannot hold the gathered rows."""
+    import ctypes
+    import torch
+    from sparse_attention_lightning_fp8_amd import _lib
+    from sparse_attention_lightning_fp8_amd import workloads as W
+    wl = W.MLA_WORKLOADS["mla_decode_b16_t16384"]
+    lib = _lib.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    ws_bytes = lib.lk_sparse_mla_workspace_size(wl.B, wl.n_idx)
+    sets = []
+    for i in range(n_sets):
+        g = torch.Generator(device=dev).manual_seed(1000 + i)
+        s = {
+            "ql": torch.randn((wl.B, 128, 512), generator=g, device=dev).to(torch.bfloat16),
+            "qr": torch.randn((wl.B, 128, 64), generator=g, device=dev).to(torch.bfloat16),
+            "kl": torch.randn((wl.B, wl.cap, 512), generator=g, device=dev).to(torch.bfloat16),
+            "kr": torch.randn((wl.B, wl.cap, 64), generator=g, device=dev).to(torch.bfloat16),
+            "idx": torch.stack([torch.randperm(wl.cap, generator=g, device=dev)[:wl.n_idx]
+                                for _ in range(wl.B)]).to(torch.int32),
+            "out": torch.empty((wl.B, 128, 512), dtype=torch.float32, device=dev),
+            "ws": torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
+        }
+        s["call"] = (s["ql"].data_ptr(), s["qr"].data_ptr(), s["kl"].data_ptr(), s["kr"].data_ptr(), wl.cap, wl.cap,
+                     s["idx"].data_ptr(), wl.B, wl.n_idx, ctypes.c_float(W.MLA_SCALE), s["out"].data_ptr(),
+                     s["ws"].data_ptr(), ws_bytes, stream)
+        sets.append(s)
+    fn = lib.lk_sparse_mla_decode
+    for i in range(warmup):
+        fn(*sets[i % n_sets]["call"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st = fn(*sets[i % n_sets]["call"])
+        if st != 0:
+            raise RuntimeError(f"lk_sparse_mla_decode returned {st}")
+    torch.cuda.synchronize()
+    call_us = (time.perf_counter() - t0) / steps * 1e6
+    evs = make_event_pairs(steps, 1)
+    for i in range(steps):
+        lib.lk_profile_next_launch(evs[i][0][0].cuda_event, evs[i][0][1].cuda_event)
+        fn(*sets[i % n_sets]["call"])
+    torch.cuda.synchronize()
+    split_us = sum(e[0][0].elapsed_time(e[0][1]) for e in evs) / steps * 1e3
+    n_sel = wl.B * wl.n_idx
+    gathered = n_sel * (512 + 64) * 2
+    algo = gathered + wl.B * 128 * (512 + 64) * 2 + wl.B * 128 * 512 * 4 + wl.B * wl.n_idx * 4
+    flops = n_sel * 128 * ((512 + 64) + 512) * 2
+    return {"call_us": call_us, "split_kernel_us": split_us, "algorithmic_bytes": algo, "flop": flops,
+            "hbm_GBps": algo / (call_us * 1e-6) / 1e9, "hbm_frac": algo / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "TFLOPs": flops / (call_us * 1e-6) / 1e12,
+            "bf16_mfma_frac": flops / (call_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+            "workspace_bytes": ws_bytes, "rotated_input_copies": n_sets}
+
+
 # ---------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl_name):
     """The oracle, single-threaded, on the same decode step (all 16 rows): key write of the
@@ -341,6 +401,12 @@ def main():
             log(f"{name}: score {pper['index_score']:.1f} us = {tf:.1f} TFLOP/s")
             del pinp
             torch.cuda.empty_cache()
+
+    if not args.no_mla:
+        log("mla_decode_b16_t16384: setting up")
+        extra["mla_decode_b16_t16384"] = time_mla(api, args.steps, args.warmup, 4, dev)
+        log(f"sparse MLA decode: {extra['mla_decode_b16_t16384']['call_us']:.1f} us per call")
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:

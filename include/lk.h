@@ -45,6 +45,9 @@ extern "C" {
 #define LK_HEADS 64         /* index heads (page "Index scores")                       */
 #define LK_TOPK_MAX_T 16384 /* longest score row lk_topk accepts (one row in LDS)      */
 #define LK_ROPE_DIM 64      /* leading features RoPE rotates (Indexer.forward excerpt)  */
+#define LK_MLA_HEADS 128    /* attention heads of the MLA decode (page "Join query parts") */
+#define LK_MLA_LATENT 512   /* latent (content) features per head and per cached row    */
+#define LK_MLA_ROPE 64      /* rotary features per head and per cached row              */
 
 typedef enum lk_status {
     LK_OK = 0,
@@ -203,6 +206,32 @@ LK_API lk_status lk_decode_score(const uint16_t *q, const float *w, int32_t head
  */
 LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, int32_t *idx,
                          hipStream_t stream);
+
+/*
+ * Sparse MLA decode attention over the indexer's selection (page "Join query parts",
+ * the MQA-decode excerpt: scores of the absorbed latent query and the rotary query
+ * against the cached latent and rotary rows, the index mask keeping only the top-k
+ * slots, softmax, weighted sum of the latent rows).  For sequence b and head h:
+ *   s_t = scale * (q_latent[b,h,:] . kv_latent[b,t,:] + q_rope[b,h,:] . kv_rope[b,t,:])
+ *   for t in I_b = { idx[b*n_idx + j] : 0 <= idx < cache_rows },
+ *   out[b,h,:] = sum_{t in I_b} softmax_t(s) * kv_latent[b,t,:];  zeros if I_b is empty.
+ *   q_latent [B][128][512], q_rope [B][128][64]: bf16 bits
+ *   kv_latent: row t of sequence b at kv_latent + (b*cache_seq_stride + t)*512 (bf16)
+ *   kv_rope:   row t of sequence b at kv_rope + (b*cache_seq_stride + t)*64 (bf16)
+ *   idx [B][n_idx] int32: distinct slots; -1 (or any value outside [0, cache_rows))
+ *   marks an unused entry, as lk_topk pads its result
+ *   out [B][128][512] float32
+ *   workspace: device memory of at least lk_sparse_mla_workspace_size(B, n_idx) bytes
+ *   (per-split partial results), owned by the caller, contents need no initialisation.
+ * Logits and the softmax run in fp32 on bf16 MFMA products; p is rounded to bf16 for
+ * the weighted sum (fp32 accumulation).  Requires cache_rows <= cache_seq_stride; all
+ * tensors 16-byte aligned except idx (4).  LK_E_SHAPE if the workspace is too small.
+ */
+LK_API size_t lk_sparse_mla_workspace_size(int32_t B, int32_t n_idx);
+LK_API lk_status lk_sparse_mla_decode(const uint16_t *q_latent, const uint16_t *q_rope, const uint16_t *kv_latent,
+                                      const uint16_t *kv_rope, int64_t cache_seq_stride, int64_t cache_rows,
+                                      const int32_t *idx, int32_t B, int32_t n_idx, float scale, float *out,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Profiling aid, outside the indexer computation: arm two HIP events for the next

@@ -33,6 +33,9 @@ SIGNATURES = {
     "lk_decode_score": (ctypes.c_int, [_p, _p, _i32, _p, _p, _p, _i64, ctypes.POINTER(LkRows), _p, _p, _p,
                                        _p, _p, _p]),
     "lk_topk": (ctypes.c_int, [_p, ctypes.POINTER(LkRows), _i32, _p, _p]),
+    "lk_sparse_mla_workspace_size": (ctypes.c_size_t, [_i32, _i32]),
+    "lk_sparse_mla_decode": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _i32, ctypes.c_float, _p, _p,
+                                            ctypes.c_size_t, _p]),
     "lk_profile_next_launch": (ctypes.c_int, [_p, _p]),
     "lk_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lk_abi_version": (_i32, []),

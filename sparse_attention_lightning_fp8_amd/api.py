@@ -215,3 +215,48 @@ def lk_topk(scores: torch.Tensor, k: int, start_pos: int = 0, seq_len: Optional[
     st = _lib.load().lk_topk(scores.data_ptr(), ctypes.byref(rows), k, idx.data_ptr(), _stream(scores))
     _lib.check("lk_topk", st)
     return idx
+
+
+MLA_HEADS, MLA_LATENT, MLA_ROPE = 128, 512, 64
+
+
+def lk_sparse_mla_decode(q_latent: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tensor,
+                         kv_rope: torch.Tensor, idx: torch.Tensor, scale: float,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sparse MLA decode attention over selected slots: q_latent [B, 128, 512] and
+    q_rope [B, 128, 64] (bf16), latent / rotary caches [>=B, cap, 512] / [>=B, cap, 64]
+    (bf16, same sequence stride in rows), idx [B, n] int32 (-1 = unused) ->
+    out [B, 128, 512] float32.  `workspace` (uint8, at least
+    lk_sparse_mla_workspace_size bytes) is allocated when not given."""
+    _need(q_latent.dtype == torch.bfloat16 and q_latent.is_contiguous() and q_latent.dim() == 3
+          and tuple(q_latent.shape[1:]) == (MLA_HEADS, MLA_LATENT), "q_latent must be contiguous bf16 [B, 128, 512]")
+    B = q_latent.shape[0]
+    _need(q_rope.dtype == torch.bfloat16 and q_rope.is_contiguous() and tuple(q_rope.shape) == (B, MLA_HEADS, MLA_ROPE),
+          "q_rope must be contiguous bf16 [B, 128, 64]")
+    _need(kv_latent.dtype == torch.bfloat16 and kv_latent.dim() == 3 and kv_latent.shape[2] == MLA_LATENT
+          and kv_latent.stride(2) == 1 and kv_latent.stride(1) == MLA_LATENT and kv_latent.shape[0] >= B,
+          "kv_latent must be bf16 [>=B, cap, 512] with contiguous rows")
+    stride = kv_latent.stride(0) // MLA_LATENT
+    _need(kv_rope.dtype == torch.bfloat16 and kv_rope.dim() == 3 and kv_rope.shape[2] == MLA_ROPE
+          and kv_rope.stride(2) == 1 and kv_rope.stride(1) == MLA_ROPE and kv_rope.shape[:2] == kv_latent.shape[:2]
+          and (kv_rope.shape[0] == 1 or kv_rope.stride(0) // MLA_ROPE == stride),
+          "kv_rope must be bf16 [.., cap, 64] sharing kv_latent's rows")
+    _need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.dim() == 2 and idx.shape[0] == B,
+          "idx must be contiguous int32 [B, n]")
+    n_idx = idx.shape[1]
+    lib = _lib.load()
+    need_ws = lib.lk_sparse_mla_workspace_size(B, n_idx)
+    if workspace is None:
+        workspace = torch.empty(max(need_ws, 16), dtype=torch.uint8, device=q_latent.device)
+    _need(workspace.is_cuda and workspace.numel() * workspace.element_size() >= need_ws, "workspace too small")
+    if out is None:
+        out = torch.empty((B, MLA_HEADS, MLA_LATENT), dtype=torch.float32, device=q_latent.device)
+    _need(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, MLA_HEADS, MLA_LATENT),
+          "bad out")
+    st = lib.lk_sparse_mla_decode(q_latent.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(), kv_rope.data_ptr(),
+                                  stride, kv_latent.shape[1], idx.data_ptr(), B, n_idx, float(scale), out.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(q_latent))
+    _lib.check("lk_sparse_mla_decode", st)
+    return out
+

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "liblk.so")
-SOURCES = ["quantize.hip", "score.hip", "topk.hip", "lk_api.hip"]
+SOURCES = ["quantize.hip", "score.hip", "topk.hip", "mla.hip", "lk_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -14,6 +14,10 @@ hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t
                                float *k_scale, int64_t cache_seq_stride, const RowsDev &rows, float *scores,
                                uint8_t *q_fp8_out, float *w_eff_out, const float *rope_cos,
                                const float *rope_sin, hipStream_t stream);
+size_t mla_workspace_bytes(int32_t B, int32_t n_idx);
+hipError_t launch_sparse_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *kv_lat,
+                             const uint16_t *kv_rope, int64_t stride, int64_t cap, const int32_t *idx, int32_t B,
+                             int32_t n_idx, float scale, float *out, void *workspace, hipStream_t stream);
 }  // namespace lk
 
 namespace lk {
@@ -211,6 +215,30 @@ LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, in
     if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(rows->seq_len, 4)) return LK_E_UNSUPPORTED;
     if ((int64_t)rows->B * rows->S > kMaxGridX) return LK_E_UNSUPPORTED;
     return from_hip(lk::launch_topk(scores, to_dev(*rows), k, idx, stream));
+}
+
+LK_API size_t lk_sparse_mla_workspace_size(int32_t B, int32_t n_idx) {
+    if (B <= 0 || n_idx <= 0) return 0;
+    return lk::mla_workspace_bytes(B, n_idx);
+}
+
+LK_API lk_status lk_sparse_mla_decode(const uint16_t *q_latent, const uint16_t *q_rope, const uint16_t *kv_latent,
+                                      const uint16_t *kv_rope, int64_t cache_seq_stride, int64_t cache_rows,
+                                      const int32_t *idx, int32_t B, int32_t n_idx, float scale, float *out,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    DisarmOnExit disarm;
+    if (B < 0 || n_idx < 0 || cache_seq_stride < 0 || cache_rows < 0) return LK_E_SHAPE;
+    if (cache_rows > cache_seq_stride) return LK_E_SHAPE;
+    if (B == 0) return LK_OK;
+    if (!q_latent || !q_rope || !out || (n_idx > 0 && (!kv_latent || !kv_rope || !idx || !workspace)))
+        return LK_E_NULL;
+    if (workspace_bytes < lk_sparse_mla_workspace_size(B, n_idx)) return LK_E_SHAPE;
+    if (!aligned(q_latent, 16) || !aligned(q_rope, 16) || !aligned(kv_latent, 16) || !aligned(kv_rope, 16) ||
+        !aligned(out, 16) || !aligned(workspace, 16) || !aligned(idx, 4))
+        return LK_E_UNSUPPORTED;
+    if (B > kMaxGridYZ) return LK_E_UNSUPPORTED;
+    return from_hip(lk::launch_sparse_mla(q_latent, q_rope, kv_latent, kv_rope, cache_seq_stride, cache_rows, idx, B,
+                                          n_idx, scale, out, workspace, stream));
 }
 
 LK_API lk_status lk_profile_next_launch(hipEvent_t start, hipEvent_t stop) {

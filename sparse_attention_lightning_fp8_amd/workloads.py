@@ -129,3 +129,50 @@ def bf16_bits(t: torch.Tensor):
     """numpy uint16 view of a bfloat16 CPU tensor's bit patterns."""
     import numpy as np
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# Sparse MLA decode (page "Join query parts"): 128 heads, 512 latent + 64 rotary
+# features, over the 2048 slots the indexer selected out of a 16384-slot cache.
+@dataclass(frozen=True)
+class MlaWorkload:
+    name: str
+    B: int
+    cap: int
+    n_idx: int
+    note: str = field(default="", compare=False)
+
+
+MLA_WORKLOADS = {
+    "mla_decode_b16_t16384": MlaWorkload("mla_decode_b16_t16384", B=16, cap=16384, n_idx=2048,
+                                         note="16 decode rows, top-2048 of 16384 cached latent rows"),
+}
+MLA_SCALE = 576 ** -0.5        # the joined 576-feature width of page "Join query parts"
+
+
+@dataclass
+class MlaInputs:
+    wl: MlaWorkload
+    q_lat: torch.Tensor            # bf16 [B, 128, 512]
+    q_rope: torch.Tensor           # bf16 [B, 128, 64]
+    kv_lat: torch.Tensor           # bf16 [B, cap, 512]
+    kv_rope: torch.Tensor          # bf16 [B, cap, 64]
+    idx: torch.Tensor              # i32  [B, n_idx], distinct slots, -1 padding
+
+
+def mla_indices(B: int, cap: int, n_idx: int, seed: int, lens=None) -> torch.Tensor:
+    """Distinct random slots per row (the shape of a top-k set), -1 beyond min(n_idx, len)."""
+    g = _gen(seed, 9)
+    out = torch.full((B, n_idx), -1, dtype=torch.int32)
+    for b in range(B):
+        L = cap if lens is None else int(lens[b])
+        k = min(n_idx, L)
+        if k > 0:
+            out[b, :k] = torch.randperm(L, generator=g)[:k].to(torch.int32)
+    return out
+
+
+def make_mla_inputs(wl: MlaWorkload, seed: int = 0, lens=None) -> MlaInputs:
+    return MlaInputs(wl, bf16_normal((wl.B, 128, 512), seed, 5), bf16_normal((wl.B, 128, 64), seed, 6),
+                     bf16_normal((wl.B, wl.cap, 512), seed, 7), bf16_normal((wl.B, wl.cap, 64), seed, 8),
+                     mla_indices(wl.B, wl.cap, wl.n_idx, seed, lens))
+

@@ -28,7 +28,8 @@ def lib():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     assert syms == sorted(["lk_quantize_keys", "lk_quantize_queries", "lk_index_score", "lk_topk",
-                           "lk_prepare", "lk_decode_score", "lk_profile_next_launch", "lk_status_string",
+                           "lk_prepare", "lk_decode_score", "lk_sparse_mla_workspace_size",
+                           "lk_sparse_mla_decode", "lk_profile_next_launch", "lk_status_string",
                            "lk_abi_version"])
 
 
@@ -139,6 +140,24 @@ def test_topk_validation(lib):
     assert f(A, rows(), 8, None, None) == E_NULL
     assert f(A + 2, rows(), 8, A, None) == E_UNSUP
     assert f(None, rows(B=0), 8, None, None) == OK
+
+
+def test_sparse_mla_validation(lib):
+    f = lib.lk_sparse_mla_decode
+    ws = lib.lk_sparse_mla_workspace_size(16, 2048)
+    assert ws == 16 * 8 * 128 * 514 * 4
+    assert lib.lk_sparse_mla_workspace_size(0, 5) == 0
+    #        qlat qrope kvl kvr stride cap  idx  B   n    scale out ws  wsb  stream
+    assert f(A, A, A, A, 16, 17, A, 1, 8, 0.1, A, A, ws, None) == E_SHAPE       # cap beyond the stride
+    assert f(A, A, A, A, 16, 16, A, -1, 8, 0.1, A, A, ws, None) == E_SHAPE
+    assert f(A, A, A, A, 16, 16, A, 1, 8, 0.1, A, A, 10, None) == E_SHAPE       # workspace too small
+    assert f(None, A, A, A, 16, 16, A, 1, 8, 0.1, A, A, ws, None) == E_NULL
+    assert f(A, A, None, A, 16, 16, A, 1, 8, 0.1, A, A, ws, None) == E_NULL
+    assert f(A, A, A, A, 16, 16, A, 1, 8, 0.1, A, None, ws, None) == E_NULL
+    assert f(A + 8, A, A, A, 16, 16, A, 1, 8, 0.1, A, A, ws, None) == E_UNSUP
+    assert f(A, A, A, A, 16, 16, A + 2, 1, 8, 0.1, A, A, ws, None) == E_UNSUP
+    assert f(A, A, A, A, 16, 16, A, 70000, 8, 0.1, A, A, 1 << 40, None) == E_UNSUP   # grid limit
+    assert f(None, None, None, None, 16, 16, None, 0, 8, 0.1, None, None, 0, None) == OK
 
 
 def test_profile_next_launch_validation(lib):
