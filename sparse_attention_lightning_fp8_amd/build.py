@@ -25,7 +25,8 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
 # Per-file flags.  The score kernels see only finite values (a documented input
 # contract), so ReLU may compile to a single v_max without IEEE NaN canonicalization;
 # their MFMA accumulators stay in VGPRs, which the epilogue reads directly.
-FILE_FLAGS = {"score.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+FILE_FLAGS = {"score.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
