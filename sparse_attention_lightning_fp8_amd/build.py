@@ -26,7 +26,7 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
 # contract), so ReLU may compile to a single v_max without IEEE NaN canonicalization;
 # their MFMA accumulators stay in VGPRs, which the epilogue reads directly.
 FILE_FLAGS = {"score.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "mla.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

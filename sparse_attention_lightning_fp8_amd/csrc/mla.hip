@@ -6,22 +6,31 @@
 // only the top-k selected slots t in I, p = softmax(s) over I, o_h = sum_t p_t c_t
 // (512 features; the up-projection that follows is outside this path).
 //
-// Split kernel: block (split, head half, b) owns 64 heads (4 waves x 16) and one
-// split of at most 256 entries of the row's index list, taken as chunks of 32 keys.
-// A chunk's latent (1 KB) and rotary (128 B) rows are gathered from HBM straight into
-// LDS by DMA (global_load_lds: one instruction moves one latent row, or eight rotary
-// rows), key-major, with each row's 16-byte chunks XOR-swizzled by the row index
-// through the source address.  Two chunk buffers alternate: the DMA of chunk c+1 is
-// in flight while chunk c is computed.  Each wave keeps its 16 heads' query (576
-// features, bf16) in registers as the A operand of v_mfma_f32_16x16x32_bf16 for
-// S = Q K^T; the P V product takes its B operand (8 consecutive keys of one latent
-// feature per lane) from the same key-major rows with two transposing LDS reads
-// (ds_read_b64_tr_b16: within 16 lanes, lane l receives element l % 4 of the 8-byte
-// pieces read by lanes 4i + l / 4).  Online softmax per wave (row max and sum over
-// the 16 lanes that hold one head's keys); p rounded to bf16 for P V; o for 16 heads
-// x 512 features accumulates in 128 registers per lane.  The split writes its
-// unnormalised o with the running max m and sum l to the workspace.
-// Combine kernel: per (b, h), o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
+// Split kernel: block (split, head half, b) owns 64 heads and one split of at most
+// 256 entries of the row's index list, taken as chunks of 32 keys.  A chunk's latent
+// (1 KB) and rotary (128 B) rows are gathered from HBM straight into LDS by DMA
+// (global_load_lds: one instruction moves one latent row, or eight rotary rows),
+// key-major, each row's 16-byte chunks XOR-swizzled by a pattern of the row index
+// through the source address.  Four chunk buffers rotate; chunk c + 2 is in flight
+// while chunk c is scored and chunk c - 1 is multiplied into o.
+// Eight waves, two per SIMD, in two roles:
+//  - score waves (0..3): wave (a, kh) holds the query of heads 32a .. 32a+31 (576
+//    features, bf16, 144 registers) and computes S^T = K Q^T with
+//    v_mfma_f32_16x16x32_bf16 for keys 16kh .. 16kh+15 of the chunk, so that each lane
+//    holds 4 keys of 2 heads and the per-head softmax bookkeeping runs twice per lane.
+//    The pair (a, 0), (a, 1) exchanges per-head chunk maxima through LDS, so both
+//    apply the same running max; each writes p (bf16) for its keys and keeps per-lane
+//    partial sums l, added up once at the end.
+//  - P V waves (4..7): wave v accumulates o for all 64 heads and latent features
+//    128v .. 128v+127 (128 registers) with v_mfma_f32_32x32x16_bf16, A = p from LDS
+//    (two 32-head tiles), B = 8 consecutive keys of one feature per lane, read from the
+//    key-major rows by two transposing LDS reads (ds_read_b64_tr_b16: within 16 lanes,
+//    lane l receives element l % 4 of the 8-byte pieces read by lanes 4i + l / 4).
+//    These reads run at about a quarter of the rate of 16-byte LDS reads (measured),
+//    so each B operand feeds both head tiles.  The P V waves also issue the DMAs.
+// The split writes its unnormalised o with the running max m (base-2 logit units)
+// and sum l to the workspace.
+// Combine kernel: per (b, h), o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 #include "lk_device.h"
 
 namespace lk {
@@ -33,14 +42,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kH = LK_MLA_HEADS;          // 128
 constexpr int kDc = LK_MLA_LATENT;        // 512
 constexpr int kDr = LK_MLA_ROPE;          // 64
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kHeadsPerBlock = 16 * kWaves;   // 64
+constexpr int kHeadsPerBlock = 64;
 constexpr int kChunk = 32;                    // keys per LDS chunk
 constexpr int kSplit = 256;                   // index-list entries per block
-constexpr int kLatRow = 2 * kDc;               // bytes per latent row in LDS (64 chunks of 16 B)
+constexpr int kBufs = 4;                      // chunk buffers in LDS
+constexpr int kLatRow = 2 * kDc;              // bytes per latent row in LDS (64 chunks of 16 B)
 constexpr int kRopeRow = 2 * kDr;             // bytes per rotary row in LDS (8 chunks of 16 B)
-static_assert(kThreads == 2 * 4 * kChunk, "8 lanes x 4 waves per 32-key chunk row set");
+constexpr int kPPitch = kChunk + 8;           // bf16 per head row of p (80 B: conflict-free reads)
 
 struct MlaArgs {
     const uint16_t *q_lat, *q_rope;           // [B][128][512], [B][128][64]
@@ -61,22 +71,6 @@ typedef void __attribute__((address_space(3))) *lptr_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// Max / sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), result in every lane.
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, __shfl_xor(x, 1, 64));
-    x = fmaxf(x, __shfl_xor(x, 2, 64));
-    x = fmaxf(x, __shfl_xor(x, 4, 64));
-    x = fmaxf(x, __shfl_xor(x, 8, 64));
-    return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
-    return x;
-}
-
 // bf16 (nearest-even) bits of a finite float.
 __device__ __forceinline__ uint32_t bf16_rne(float v) {
     const uint32_t u = __float_as_uint(v);
@@ -93,213 +87,372 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory", "m0");
 }
 
-// Gather chunk c (keys sidx[32c .. 32c+31]) into lat / rope: wave w moves latent rows
-// 8w .. 8w+7 (one DMA each) and rotary rows 8w .. 8w+7 (one DMA).  Row r's 16-byte
-// chunk j lands in slot j ^ (r % 16) (latent) or j ^ (r % 8) (rotary).
+// XOR pattern of latent row r: r % 16 rotated right by one bit.  Reads of one chunk
+// position from 16 consecutive rows (the S operand, ds_read_b128) then hit 16 distinct
+// 16-byte slots at the full LDS rate; the transposing reads of the P V operand run at
+// about a quarter of that rate whatever the pattern (measured), this one included.
+__device__ __forceinline__ int lat_swizzle(int r) { return ((r & 1) << 3) | ((r >> 1) & 7); }
+
+// Gather chunk c (keys sidx[32c .. 32c+31]) into lat / rope; issued by the P V waves,
+// whose phases have slack: P V wave v moves latent rows 8v .. 8v+7 (one DMA each) and
+// rotary rows 8v .. 8v+7 (one DMA).  Row r's 16-byte chunk j lands in slot
+// j ^ lat_swizzle(r) (latent) or j ^ (r % 8) (rotary).
+constexpr int kDma = 9;                        // DMA instructions per chunk per P V wave
 __device__ __forceinline__ void gather_chunk(const MlaArgs &a, int b, const int32_t *sidx, int c, uint8_t *lat,
-                                             uint8_t *rope, int wave, int lane) {
+                                             uint8_t *rope, int v, int lane) {
+    const int4 r0 = *reinterpret_cast<const int4 *>(&sidx[c * kChunk + 8 * v]);
+    const int4 r1 = *reinterpret_cast<const int4 *>(&sidx[c * kChunk + 8 * v + 4]);
+    const int rr = sidx[c * kChunk + 8 * v + (lane >> 3)];
+    const int rows[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    const uint8_t *kl = reinterpret_cast<const uint8_t *>(a.kv_lat) + (int64_t)b * a.stride * kLatRow;
+    const uint8_t *kr = reinterpret_cast<const uint8_t *>(a.kv_rope) + (int64_t)b * a.stride * kRopeRow;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        const int r = 8 * wave + j;
-        const int row = sidx[c * kChunk + r];
-        const int64_t g = (int64_t)b * a.stride + (row < 0 ? 0 : row);
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(a.kv_lat) + g * kLatRow + 16 * (lane ^ (r & 15));
-        dma16(src, lat + r * kLatRow);
+        const int r = 8 * v + j;
+        const int64_t row = rows[j] < 0 ? 0 : rows[j];
+        dma16(kl + row * kLatRow + 16 * (lane ^ lat_swizzle(r)), lat + r * kLatRow);
     }
-    const int r = 8 * wave + (lane >> 3);
-    const int row = sidx[c * kChunk + r];
-    const int64_t g = (int64_t)b * a.stride + (row < 0 ? 0 : row);
-    const uint8_t *src = reinterpret_cast<const uint8_t *>(a.kv_rope) + g * kRopeRow + 16 * ((lane & 7) ^ (r & 7));
-    dma16(src, rope + 8 * wave * kRopeRow);
-}
-
-// Per-lane LDS byte offsets of the swizzled rows, fixed for the whole kernel.  Every
-// read below is one of these plus a constant: XOR with the row index only touches the
-// low four bits of a 16-byte chunk number, so chunk 16 j + c' of a row lies 256 j
-// bytes after chunk c'.
-struct LdsOffsets {
-    uint32_t s_lat[4];       // S: latent row r16, chunk 4 kk + g4 (kk = k % 4)
-    uint32_t s_rope[2];      // S: rotary row r16, chunk 4 kk + g4
-    uint32_t pv[2][8];       // P V: transposing read h, feature chunk pair n' (n = 8 j + n')
-};
-
-__device__ __forceinline__ LdsOffsets lds_offsets(int lane) {
-    const int r16 = lane & 15, g4 = lane >> 4, sq = r16 & 3;
-    LdsOffsets t;
-#pragma unroll
-    for (int kk = 0; kk < 4; kk++) t.s_lat[kk] = r16 * kLatRow + 16 * ((4 * kk + g4) ^ r16);
-#pragma unroll
-    for (int kk = 0; kk < 2; kk++) t.s_rope[kk] = r16 * kRopeRow + 16 * ((4 * kk + g4) ^ (r16 & 7));
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const int row = 8 * g4 + 4 * h + (r16 >> 2);
-#pragma unroll
-        for (int n = 0; n < 8; n++) t.pv[h][n] = row * kLatRow + 16 * ((2 * n + (sq >> 1)) ^ (row & 15)) + 8 * (sq & 1);
-    }
-    return t;
+    const int r = 8 * v + (lane >> 3);
+    const int64_t row = rr < 0 ? 0 : rr;
+    dma16(kr + row * kRopeRow + 16 * ((lane & 7) ^ (r & 7)), rope + 8 * v * kRopeRow);
 }
 
 // Raise the running max only when a chunk exceeds it by more than 2^8 (base-2 logits):
-// p = 2^(x - m) then stays below 2^8, and the rescale of o (128 registers) runs on
-// few chunks.  The result does not depend on which m is used.
+// p = 2^(x - m) then stays below 2^8, and the rescale of o runs on few chunks.  The
+// result does not depend on which m is used.
 constexpr float kLazyMax = 8.f;
 
-// One chunk of S = Q K^T, online softmax and O += P V for this wave's 16 heads.
-__device__ __forceinline__ void chunk_compute(const bf16x8 qa[18], const uint8_t *lat, const uint8_t *rope,
-                                              const LdsOffsets &off, const int32_t *sidx, int c, float sl2,
-                                              float m[4], float l[4], f32x4 o[kDc / 16], uint16_t *ptw, int lane) {
-    const int r16 = lane & 15, g4 = lane >> 4;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+struct SharedMem {
+    uint8_t lat[kBufs][kChunk * kLatRow];     // 128 KB
+    uint8_t rope[kBufs][kChunk * kRopeRow];   // 16 KB
+    uint16_t p[2][kHeadsPerBlock * kPPitch];  // p of the chunk last scored, bf16 [head][key]
+    float alpha[2][kHeadsPerBlock];           // o rescale factor per head for that chunk
+    int32_t rescale[2][2];                    // any alpha != 1, per head group
+    float part[kHeadsPerBlock][8];            // per head: chunk maxima (later sums) of the 8 lane groups of a pair
+    int32_t sidx[kSplit];
+};
+
+// ---- score wave: S^T = K Q^T for 16 keys x 32 heads, softmax bookkeeping
+struct ScoreState {
+    bf16x8 qa[2][18];                         // [head tile][K-step]
+    uint32_t off_lat[4], off_rope[2];         // swizzled LDS offsets (see score_chunk)
+    float m[2], l[2];                         // head 16t + r16 of the group; l: this lane's 4 keys
+};
+
+// Lane (r16, g4) of score wave (a, kh) holds keys 16kh + 4g4 + i (i = 0..3) of heads
+// 16t + r16 (t = 0, 1) of group a.
+__device__ __forceinline__ void score_chunk(ScoreState &st, SharedMem &sm, int buf, int c, int wave, int lane,
+                                            float sl2, float x[2][4]) {
+    const int r16 = lane & 15, g4 = lane >> 4, kh = wave & 1, grp = wave >> 1;
+    const uint8_t *lat = sm.lat[buf] + kh * 16 * kLatRow;
+    const uint8_t *rope = sm.rope[buf] + kh * 16 * kRopeRow;
+    f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // A operand of K-step k: key 16kh + r16, features 32k + 8 g4 .. +7; chunk 16 j + c'
+    // of a row lies 256 j bytes after chunk c' (the XOR only touches the low 4 bits).
 #pragma unroll
     for (int k = 0; k < 18; k++) {
-        const uint8_t *p0 = k < 16 ? lat + off.s_lat[k % 4] + 256 * (k / 4) : rope + off.s_rope[k - 16];
-        const int second = k < 16 ? 16 * kLatRow : 16 * kRopeRow;
-        const uint4 b0 = *reinterpret_cast<const uint4 *>(p0);
-        const uint4 b1 = *reinterpret_cast<const uint4 *>(p0 + second);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[k], as_bf16x8(b0), s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[k], as_bf16x8(b1), s1, 0, 0, 0);
+        const uint8_t *p0 = k < 16 ? lat + st.off_lat[k % 4] + 256 * (k / 4) : rope + st.off_rope[k - 16];
+        const bf16x8 kb = as_bf16x8(*reinterpret_cast<const uint4 *>(p0));
+        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, st.qa[0][k], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, st.qa[1][k], s[1], 0, 0, 0);
     }
-    // lane holds keys r16 (s0) and 16 + r16 (s1) of heads 4 g4 + i
-    const bool ok0 = sidx[c * kChunk + r16] >= 0, ok1 = sidx[c * kChunk + 16 + r16] >= 0;
-    float alpha[4];
-    bool rescale = false;
+    const int4 ids = *reinterpret_cast<const int4 *>(&sm.sidx[c * kChunk + 16 * kh + 4 * g4]);
+    const bool ok[4] = {ids.x >= 0, ids.y >= 0, ids.z >= 0, ids.w >= 0};
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float x0 = ok0 ? s0[i] * sl2 : -__builtin_inff();
-        const float x1 = ok1 ? s1[i] * sl2 : -__builtin_inff();
-        const float cm = row16_max(fmaxf(x0, x1));
-        alpha[i] = 1.f;
-        if (cm > m[i] + kLazyMax) {                            // also when m is -inf and cm is finite
-            alpha[i] = exp2f(m[i] - cm);                       // 0 when m was -inf
-            m[i] = cm;
-            rescale = true;
+    for (int t = 0; t < 2; t++) {
+        float lm = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            x[t][i] = ok[i] ? s[t][i] * sl2 : -__builtin_inff();
+            lm = fmaxf(lm, x[t][i]);
         }
-        float p0 = 0.f, p1 = 0.f;
-        if (m[i] != -__builtin_inff()) {
-            p0 = exp2f(x0 - m[i]);
-            p1 = exp2f(x1 - m[i]);
+        sm.part[32 * grp + 16 * t + r16][4 * kh + g4] = lm;
+    }
+}
+
+// After the pair's maxima are in LDS: running max, p, sums.
+__device__ __forceinline__ void softmax_chunk(ScoreState &st, SharedMem &sm, int pbuf, int wave, int lane,
+                                              const float x[2][4]) {
+    const int r16 = lane & 15, g4 = lane >> 4, kh = wave & 1, grp = wave >> 1;
+    bool any = false;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        const int hb = 32 * grp + 16 * t + r16;                 // head within the block
+        const float4 c0 = *reinterpret_cast<const float4 *>(&sm.part[hb][0]);
+        const float4 c1 = *reinterpret_cast<const float4 *>(&sm.part[hb][4]);
+        const float cm = fmaxf(fmaxf(fmaxf(c0.x, c0.y), fmaxf(c0.z, c0.w)), fmaxf(fmaxf(c1.x, c1.y), fmaxf(c1.z, c1.w)));
+        float alpha = 1.f;
+        if (cm > st.m[t] + kLazyMax) {                          // also when m is -inf and cm is finite
+            alpha = __builtin_amdgcn_exp2f(st.m[t] - cm);       // 0 when m was -inf
+            st.m[t] = cm;
+            any = true;
         }
-        const uint32_t q0 = bf16_rne(p0), q1 = bf16_rne(p1);
-        l[i] = l[i] * alpha[i] + row16_sum(__uint_as_float(q0 << 16) + __uint_as_float(q1 << 16));
-        ptw[(4 * g4 + i) * kChunk + r16] = (uint16_t)q0;
-        ptw[(4 * g4 + i) * kChunk + 16 + r16] = (uint16_t)q1;
+        // m is -inf only while every key so far is masked: then p = 2^(-inf) = 0
+        const float mref = st.m[t] == -__builtin_inff() ? 0.f : st.m[t];
+        uint32_t q[4];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            q[i] = bf16_rne(__builtin_amdgcn_exp2f(x[t][i] - mref));
+            sum += __uint_as_float(q[i] << 16);
+        }
+        st.l[t] = st.l[t] * alpha + sum;
+        *reinterpret_cast<uint2 *>(&sm.p[pbuf][hb * kPPitch + 16 * kh + 4 * g4]) =
+            make_uint2(q[0] | (q[1] << 16), q[2] | (q[3] << 16));
+        if (kh == 0 && g4 == 0) sm.alpha[pbuf][hb] = alpha;
     }
-    if (__any(rescale)) {
-#pragma unroll
-        for (int n = 0; n < kDc / 16; n++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) o[n][i] *= alpha[i];
+    if (kh == 0) {
+        const bool wany = __any(any);
+        if (lane == 0) sm.rescale[pbuf][grp] = wany;
     }
-    // O += P V.  A = P (lane: head r16, keys 8 g4 .. 8 g4 + 7).  B for tile n: keys
-    // 8 g4 + 4h + i of feature 16 n + r16, from transposing reads in which source
-    // lane r16 of this 16-lane group points at row 8 g4 + 4h + r16 / 4, features
-    // 16 n + 4 (r16 % 4) .. + 3.
-    const bf16x8 pa = as_bf16x8(*reinterpret_cast<const uint4 *>(ptw + r16 * kChunk + 8 * g4));
+}
+
+// ---- P V wave: o[64 heads][128 features] += P V
+struct PvState {
+    float o[2][4][16];                        // [head tile][feature tile][register]
+    uint32_t off[2][4];                       // transposing-read offsets [h'][feature tile]
+};
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void pv_rescale(PvState &st, const SharedMem &sm, int pbuf, int lane) {
 #pragma unroll
-    for (int n = 0; n < kDc / 16; n++) {
-        v4i16 half[2];
+    for (int mt = 0; mt < 2; mt++) {
+        if (!sm.rescale[pbuf][mt]) continue;
+        // register i of a tile holds head row 8 (i / 4) + 4 (lane / 32) + i % 4
+        float al[16];
 #pragma unroll
-        for (int h = 0; h < 2; h++)
-            half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lptr_t)(lat + off.pv[h][n % 8] + 256 * (n / 8)));
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[n], 0, 0, 0);
+        for (int j = 0; j < 4; j++) {
+            const float4 v = *reinterpret_cast<const float4 *>(&sm.alpha[pbuf][32 * mt + 8 * j + 4 * (lane >> 5)]);
+            al[4 * j] = v.x;
+            al[4 * j + 1] = v.y;
+            al[4 * j + 2] = v.z;
+            al[4 * j + 3] = v.w;
+        }
+#pragma unroll
+        for (int n = 0; n < 4; n++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) st.o[mt][n][i] *= al[i];
     }
+}
+
+// Feature tiles n0, n0 + 1 (32 features each) of chunk `buf` with p from `pbuf`.
+__device__ __forceinline__ void pv_tiles(PvState &st, const SharedMem &sm, int buf, int pbuf, int lane, int n0) {
+    const uint8_t *lat = sm.lat[buf];
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+        // A: head 32 mt + lane % 32, keys 16 ks + 8 (lane / 32) .. +7
+        bf16x8 pa[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++)
+            pa[mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                &sm.p[pbuf][(32 * mt + (lane & 31)) * kPPitch + 16 * ks + 8 * (lane >> 5)]));
+#pragma unroll
+        for (int nn = 0; nn < 2; nn++) {
+            const int n = n0 + nn;
+            v4i16 hv[2];
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+                hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lptr_t)(lat + st.off[h][n] + ks * 16 * kLatRow));
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++) {
+                f32x16 acc;
+#pragma unroll
+                for (int i = 0; i < 16; i++) acc[i] = st.o[mt][n][i];
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[mt], vb, acc, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 16; i++) st.o[mt][n][i] = acc[i];
+            }
+        }
+    }
+}
+
+// Block-level context shared by both roles.
+struct SplitCtx {
+    int b, split, half, nch, nk, k0, wave, lane, grp, hbase;
+    float sl2;
+};
+
+// Barrier sequence, identical in both roles: slot list filled (the score waves' query
+// loads overlap it), chunks 0 and 1 issued with chunk 0 landed, then two per iteration
+// c = 0 .. nch (after the chunk maxima, after chunk c + 1 has landed), and one before
+// the sums are combined.  Iteration c scores chunk c and multiplies chunk c - 1; the
+// DMA of chunk c + 2 goes into the buffer of chunk c - 2, free since iteration c - 1.
+// Only the P V waves issue DMAs, and they issue no other global loads, so vmcnt counts
+// exactly their DMAs.
+
+__device__ __forceinline__ void score_role(const MlaArgs &a, SharedMem &sm, const SplitCtx &x) {
+    const int r16 = x.lane & 15, g4 = x.lane >> 4;
+    ScoreState ss;
+    // Query fragments: A operand of head tile t, K-step k (features 32k .. 32k+31; k >= 16: rotary).
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        const int64_t h = (int64_t)x.b * kH + x.hbase + 16 * t + r16;
+        const uint16_t *ql = a.q_lat + h * kDc;
+        const uint16_t *qr = a.q_rope + h * kDr;
+#pragma unroll
+        for (int k = 0; k < 16; k++) ss.qa[t][k] = as_bf16x8(*reinterpret_cast<const uint4 *>(ql + 32 * k + 8 * g4));
+#pragma unroll
+        for (int k = 0; k < 2; k++) ss.qa[t][16 + k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qr + 32 * k + 8 * g4));
+        ss.m[t] = -__builtin_inff();
+        ss.l[t] = 0.f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) ss.off_lat[kk] = r16 * kLatRow + 16 * ((4 * kk + g4) ^ lat_swizzle(r16));
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) ss.off_rope[kk] = r16 * kRopeRow + 16 * ((4 * kk + g4) ^ (r16 & 7));
+    __syncthreads();                                           // slot list (and the query is loaded)
+    __syncthreads();                                           // chunk 0 in LDS
+    float xs[2][4];
+    for (int c = 0; c <= x.nch; c++) {
+        if (c < x.nch) score_chunk(ss, sm, c % kBufs, c, x.wave, x.lane, x.sl2, xs);
+        __syncthreads();                                       // chunk maxima
+        if (c < x.nch) softmax_chunk(ss, sm, c & 1, x.wave, x.lane, xs);
+        __syncthreads();                                       // chunk c + 1 in LDS
+    }
+    // sums: every lane group of the pair leaves its partial l in LDS; wave (a, 0)
+    // adds them up and writes m and l
+#pragma unroll
+    for (int t = 0; t < 2; t++) sm.part[32 * x.grp + 16 * t + r16][4 * (x.wave & 1) + g4] = ss.l[t];
+    __syncthreads();
+    if (!(x.wave & 1) && g4 == 0) {
+        float *mp = a.ml_part + (((int64_t)x.b * a.nsplit + x.split) * kH + x.hbase) * 2;
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int hh = 16 * t + r16;
+            const float4 c0 = *reinterpret_cast<const float4 *>(&sm.part[32 * x.grp + hh][0]);
+            const float4 c1 = *reinterpret_cast<const float4 *>(&sm.part[32 * x.grp + hh][4]);
+            mp[2 * hh] = ss.m[t];
+            mp[2 * hh + 1] = ((c0.x + c0.y) + (c0.z + c0.w)) + ((c1.x + c1.y) + (c1.z + c1.w));
+        }
+    }
+}
+
+__device__ __forceinline__ void pv_role(const MlaArgs &a, SharedMem &sm, const SplitCtx &x) {
+    const int lane = x.lane, r16 = lane & 15;
+    const int v = x.wave - 4;
+    PvState ps;
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int n = 0; n < 4; n++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) ps.o[mt][n][i] = 0.f;
+    // Transposing read h' for feature tile n, K-step ks: source lane s = lane % 16 of
+    // 16-lane group q = lane / 16 points at key row 16 ks + 8 (q / 2) + 4 h' + s / 4,
+    // features 128 v + 32 n + 16 (q % 2) + 4 (s % 4) .. +3, so lane r of the group
+    // receives feature ... + r, keys ... + 4h' + i.  The row's low 4 bits do not depend
+    // on ks: offsets differ by 16 KB per ks.
+    {
+        const int q = lane >> 4, sq = r16 & 3;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int row = 8 * (q >> 1) + 4 * h + (r16 >> 2);
+#pragma unroll
+            for (int n = 0; n < 4; n++) {
+                const int ch = 16 * v + 4 * n + 2 * (q & 1) + (sq >> 1);
+                ps.off[h][n] = row * kLatRow + 16 * (ch ^ lat_swizzle(row)) + 8 * (sq & 1);
+            }
+        }
+    }
+    // This split's slice of the index list; unused or out-of-range entries become -1.
+    {
+        const int i = threadIdx.x - 256;
+        const int v0 = i < x.nk ? a.idx[(int64_t)x.b * a.n_idx + x.k0 + i] : -1;
+        sm.sidx[i] = (v0 >= 0 && v0 < a.cap) ? v0 : -1;
+    }
+    __syncthreads();                                           // slot list
+    gather_chunk(a, x.b, sm.sidx, 0, sm.lat[0], sm.rope[0], v, lane);
+    __builtin_amdgcn_s_waitcnt(0x3F70);                        // vmcnt(0): chunk 0
+    if (x.nch > 1) gather_chunk(a, x.b, sm.sidx, 1, sm.lat[1], sm.rope[1], v, lane);
+    __syncthreads();                                           // chunk 0 in LDS
+    for (int c = 0; c <= x.nch; c++) {
+        const bool more = c + 2 < x.nch;
+        if (more) gather_chunk(a, x.b, sm.sidx, c + 2, sm.lat[(c + 2) % kBufs], sm.rope[(c + 2) % kBufs], v, lane);
+        if (c >= 1) {
+            pv_rescale(ps, sm, (c - 1) & 1, lane);
+            pv_tiles(ps, sm, (c - 1) % kBufs, (c - 1) & 1, lane, 0);
+        }
+        __syncthreads();                                       // chunk maxima
+        if (c >= 1) pv_tiles(ps, sm, (c - 1) % kBufs, (c - 1) & 1, lane, 2);
+        if (more) __builtin_amdgcn_s_waitcnt(0x3F70 | kDma);   // chunk c + 1 (all but c + 2's DMAs)
+        else __builtin_amdgcn_s_waitcnt(0x3F70);
+        __syncthreads();                                       // chunk c + 1 in LDS
+    }
+    __syncthreads();
+    // register i of a tile holds head row 8 (i / 4) + 4 (lane / 32) + i % 4, feature lane % 32
+    float *op = a.o_part + (((int64_t)x.b * a.nsplit + x.split) * kH + x.half * kHeadsPerBlock) * kDc + 128 * v + (lane & 31);
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int n = 0; n < 4; n++)
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                op[(int64_t)(32 * mt + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4)) * kDc + 32 * n] = ps.o[mt][n][i];
 }
 
 __global__ void __launch_bounds__(kThreads) mla_split_kernel(MlaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lat[2][kChunk * kLatRow];
-    __shared__ __attribute__((aligned(16))) uint8_t rope[2][kChunk * kRopeRow];
-    __shared__ __attribute__((aligned(16))) uint16_t pt[kWaves][16 * kChunk];
-    __shared__ int32_t sidx[kSplit];
-    const int tid = threadIdx.x, lane = __lane_id(), wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int split = blockIdx.x, half = blockIdx.y, b = blockIdx.z;
-    const int h0 = half * kHeadsPerBlock + wave * 16;          // this wave's first head
-    const int k0 = split * kSplit;
-    const int nk = min(kSplit, a.n_idx - k0);                  // >= 1 by the grid
-    const int r16 = lane & 15, g4 = lane >> 4;
-
-    // This split's slice of the index list; unused or out-of-range entries become -1.
-    for (int i = tid; i < kSplit; i += kThreads) {
-        int v = i < nk ? a.idx[(int64_t)b * a.n_idx + k0 + i] : -1;
-        sidx[i] = (v >= 0 && v < a.cap) ? v : -1;
-    }
-    // Query fragments: A operand of K-step k (features 32k .. 32k+31; k >= 16: rotary).
-    bf16x8 qa[18];
-    {
-        const uint16_t *ql = a.q_lat + ((int64_t)b * kH + h0 + r16) * kDc;
-        const uint16_t *qr = a.q_rope + ((int64_t)b * kH + h0 + r16) * kDr;
-#pragma unroll
-        for (int k = 0; k < 16; k++) qa[k] = as_bf16x8(*reinterpret_cast<const uint4 *>(ql + 32 * k + 8 * g4));
-#pragma unroll
-        for (int k = 0; k < 2; k++) qa[16 + k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qr + 32 * k + 8 * g4));
-    }
-    f32x4 o[kDc / 16];
-#pragma unroll
-    for (int n = 0; n < kDc / 16; n++) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m[4], l[4];                                          // heads 4 * g4 + i of this wave
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        m[i] = -__builtin_inff();
-        l[i] = 0.f;
-    }
-    const float sl2 = a.scale * 1.4426950408889634f;           // logits in base-2 units
-    __syncthreads();                                           // sidx
-
-    const int nchunks = (nk + kChunk - 1) / kChunk;
-    const LdsOffsets off = lds_offsets(lane);
-    // One barrier per chunk: it finds chunk c's DMA landed (each wave waits for its own
-    // before it) and every wave done with chunk c - 1, whose buffer then takes chunk c + 1.
-    // One barrier per chunk: before it each wave waits for its own DMAs of chunk c, after
-    // it every wave is done with chunk c - 1, whose buffer then takes chunk c + 1.
-    gather_chunk(a, b, sidx, 0, lat[0], rope[0], wave, lane);
-    for (int c = 0; c < nchunks; c++) {
-        const int cur = c & 1;
-        __builtin_amdgcn_s_waitcnt(0x3F70);                    // vmcnt(0): chunk c is in LDS
-        __syncthreads();
-        if (c + 1 < nchunks) gather_chunk(a, b, sidx, c + 1, lat[cur ^ 1], rope[cur ^ 1], wave, lane);
-        chunk_compute(qa, lat[cur], rope[cur], off, sidx, c, sl2, m, l, o, pt[wave], lane);
-    }
-    // ---- partials: unnormalised o, running max (base-2 units) and sum per head
-    float *op = a.o_part + (((int64_t)b * a.nsplit + split) * kH + h0) * kDc;
-#pragma unroll
-    for (int n = 0; n < kDc / 16; n++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) op[(int64_t)(4 * g4 + i) * kDc + 16 * n + r16] = o[n][i];
-    if (r16 == 0) {
-        float *mp = a.ml_part + (((int64_t)b * a.nsplit + split) * kH + h0) * 2;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            mp[2 * (4 * g4 + i)] = m[i];
-            mp[2 * (4 * g4 + i) + 1] = l[i];
-        }
-    }
+    __shared__ __attribute__((aligned(16))) SharedMem sm;
+    SplitCtx x;
+    x.split = blockIdx.x;
+    x.half = blockIdx.y;
+    x.b = blockIdx.z;
+    x.lane = __lane_id();
+    x.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    x.grp = (x.wave & 3) >> 1;                                 // head group: heads 32 grp .. +31 of the block
+    x.hbase = x.half * kHeadsPerBlock + 32 * x.grp;
+    x.sl2 = a.scale * 1.4426950408889634f;                     // logits in base-2 units
+    x.k0 = x.split * kSplit;
+    x.nk = min(kSplit, a.n_idx - x.k0);                        // >= 1 by the grid
+    x.nch = (x.nk + kChunk - 1) / kChunk;
+    if (x.wave < 4) score_role(a, sm, x);
+    else pv_role(a, sm, x);
 }
 
-// One block per (b, head): 256 threads x 2 features.
+// One block per (b, two heads): 128 threads x 4 features per head.  Splits are taken
+// eight at a time with every load of the group issued together (out-of-range splits
+// read the last one and get weight 0), merged into a running max / sum.
 __global__ void __launch_bounds__(256) mla_combine_kernel(MlaArgs a) {
-    const int h = blockIdx.x, b = blockIdx.y;
-    float M = -__builtin_inff();
-    for (int s = 0; s < a.nsplit; s++) {
-        const float ms = a.ml_part[(((int64_t)b * a.nsplit + s) * kH + h) * 2];
-        M = fmaxf(M, ms);
-    }
-    float den = 0.f, acc0 = 0.f, acc1 = 0.f;
-    const int c = 2 * threadIdx.x;
-    if (M != -__builtin_inff()) {
-        for (int s = 0; s < a.nsplit; s++) {
-            const float *ml = a.ml_part + (((int64_t)b * a.nsplit + s) * kH + h) * 2;
-            const float ms = ml[0];
-            if (ms == -__builtin_inff()) continue;
-            const float wgt = exp2f(ms - M);
-            den += wgt * ml[1];
-            const float2 v = *reinterpret_cast<const float2 *>(a.o_part + (((int64_t)b * a.nsplit + s) * kH + h) * kDc + c);
-            acc0 += wgt * v.x;
-            acc1 += wgt * v.y;
+    const int h = 2 * blockIdx.x + (threadIdx.x >> 7), b = blockIdx.y;
+    const int f = 4 * (threadIdx.x & 127);
+    float M = -__builtin_inff(), den = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < a.nsplit; s0 += 8) {
+        float ms[8], ls[8];
+        float4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int64_t row = ((int64_t)b * a.nsplit + min(s0 + j, a.nsplit - 1)) * kH + h;
+            const float2 ml = *reinterpret_cast<const float2 *>(a.ml_part + row * 2);
+            ms[j] = s0 + j < a.nsplit ? ml.x : -__builtin_inff();
+            ls[j] = ml.y;
+            v[j] = *reinterpret_cast<const float4 *>(a.o_part + row * kDc + f);
         }
+        float gm = M;
+#pragma unroll
+        for (int j = 0; j < 8; j++) gm = fmaxf(gm, ms[j]);
+        if (gm == -__builtin_inff()) continue;                  // nothing valid yet
+        const float r = exp2f(M - gm);                          // 0 when M was -inf
+        den *= r;
+        acc.x *= r;
+        acc.y *= r;
+        acc.z *= r;
+        acc.w *= r;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float w = exp2f(ms[j] - gm);                  // 0 for empty or padding splits
+            den += w * ls[j];
+            acc.x += w * v[j].x;
+            acc.y += w * v[j].y;
+            acc.z += w * v[j].z;
+            acc.w += w * v[j].w;
+        }
+        M = gm;
     }
-    float2 r = make_float2(0.f, 0.f);
-    if (den > 0.f) r = make_float2(acc0 / den, acc1 / den);
-    *reinterpret_cast<float2 *>(a.out + ((int64_t)b * kH + h) * kDc + c) = r;
+    float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (den > 0.f) res = make_float4(acc.x / den, acc.y / den, acc.z / den, acc.w / den);
+    *reinterpret_cast<float4 *>(a.out + ((int64_t)b * kH + h) * kDc + f) = res;
 }
 
 }  // namespace
@@ -326,12 +479,13 @@ hipError_t launch_sparse_mla(const uint16_t *q_lat, const uint16_t *q_rope, cons
     a.o_part = static_cast<float *>(workspace);
     a.ml_part = a.o_part + (int64_t)B * a.nsplit * kH * kDc;
     a.out = out;
+    if (cap == 0) a.nsplit = 0;                               // no valid slot: every output row is zero
     if (a.nsplit > 0) {
         hipError_t e = launch(mla_split_kernel, dim3((unsigned)a.nsplit, kH / kHeadsPerBlock, (unsigned)B),
                               dim3(kThreads), 0u, stream, a);
         if (e != hipSuccess) return e;
     }
-    return launch(mla_combine_kernel, dim3(kH, (unsigned)B), dim3(kDc / 2), 0u, stream, a);
+    return launch(mla_combine_kernel, dim3(kH / 2, (unsigned)B), dim3(256), 0u, stream, a);
 }
 
 }  // namespace lk
