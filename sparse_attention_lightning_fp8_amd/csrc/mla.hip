@@ -79,12 +79,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
 
 // One 16-byte-per-lane DMA from global memory into LDS at lds + 16 * lane.  Written as
 // inline asm so that the compiler does not make later LDS reads wait for it (it cannot
-// tell the two chunk buffers apart); the caller waits with vmcnt before the barrier
-// that publishes the data.  M0 holds the LDS base; an LDS DMA needs one wait state
-// after M0 is written.
+// tell the chunk buffers apart); the caller waits with vmcnt before the barrier that
+// publishes the data.  The LDS base is an input bound to M0, which the compiler writes;
+// an LDS DMA needs one wait state after M0 is written, hence the s_nop.
 __device__ __forceinline__ void dma16(const void *src, const void *lds) {
     const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lptr_t)lds);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
 }
 
 // XOR pattern of latent row r: r % 16 rotated right by one bit.  Reads of one chunk
