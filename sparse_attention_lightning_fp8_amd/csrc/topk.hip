@@ -181,6 +181,15 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
     const int rem = n - 4 * tid;                       // element e is valid iff its offset < rem
     const int wave_rem = n - 4 * 64 * wave;            // the same for the wave's first lane
     auto live = [&](int j) { return 4 * kThreads * j < wave_rem; };
+    if (vec && rem > 4 * kThreads * 3 + 3) {
+        // Every element of this thread is valid: four unconditional loads, all in flight
+        // together (under the branches below each one would be waited for alone).
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float4 x = *reinterpret_cast<const float4 *>(src + 4 * tid + 4 * kThreads * j);
+            v[4 * j] = x.x; v[4 * j + 1] = x.y; v[4 * j + 2] = x.z; v[4 * j + 3] = x.w;
+        }
+    } else {
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int o = 4 * kThreads * j;
@@ -200,6 +209,7 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
             }
         }
         v[4 * j] = x.x; v[4 * j + 1] = x.y; v[4 * j + 2] = x.z; v[4 * j + 3] = x.w;
+    }
     }
 
     // 1. Row range (NaN entries are ignored by fmaxf / fminf).
