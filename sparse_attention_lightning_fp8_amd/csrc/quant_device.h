@@ -45,6 +45,26 @@ __device__ __forceinline__ lk_v2i16 encode_e4m3_pair(lk_v2i16 old, float a, floa
     return __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, a, b, 1.0f, kHi);
 }
 
+// A rotated feature (its exact Hadamard sum) times 128^-0.5, rounded once to bf16; an
+// exact zero sum is +0.
+__device__ __forceinline__ double scale_round(double r) {
+#pragma clang fp contract(off)
+    return round_to_bf16((r == 0.0 ? 0.0 : r) * kRotScale);
+}
+
+// Smallest j >= -126 with amax <= 448 * 2^j.  amax = f * 2^E with f in [0.5, 1):
+// j = E - 9 if f <= 0.875 (448 = 0.875 * 2^9), else E - 8.
+__device__ __forceinline__ int scale_exponent(double amax) {
+    int j = -126;
+    if (amax > 0.0) {
+        const int E = __builtin_amdgcn_frexp_exp(amax);
+        const double f = __builtin_amdgcn_frexp_mant(amax);
+        j = E - 9 + (f > 0.875 ? 1 : 0);
+        j = j < -126 ? -126 : j;
+    }
+    return j;
+}
+
 // Quantize the row owned by this 8-lane group.  `in` holds the lane's 16 bf16 bit
 // patterns (8 dwords).  Returns the 16 codes packed in 4 dwords and the exponent j.
 __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t out[4], int &j_out) {
@@ -81,22 +101,12 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
     double amax = 0.0;
 #pragma unroll
     for (int e = 0; e < 16; e++) {
-        double r = x[e] == 0.0 ? 0.0 : x[e];   // an exact zero sum is +0
-        double y = round_to_bf16(r * kRotScale);
-        x[e] = y;
-        amax = __builtin_fmax(amax, __builtin_fabs(y));
+        x[e] = scale_round(x[e]);
+        amax = __builtin_fmax(amax, __builtin_fabs(x[e]));
     }
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) amax = __builtin_fmax(amax, __shfl_xor(amax, m, 64));
-    // Smallest j >= -126 with amax <= 448 * 2^j.  amax = f * 2^E with f in [0.5, 1):
-    // j = E - 9 if f <= 0.875 (448 = 0.875 * 2^9), else E - 8.
-    int j = -126;
-    if (amax > 0.0) {
-        int E = __builtin_amdgcn_frexp_exp(amax);
-        double f = __builtin_amdgcn_frexp_mant(amax);
-        j = E - 9 + (f > 0.875 ? 1 : 0);
-        j = j < -126 ? -126 : j;
-    }
+    const int j = scale_exponent(amax);
     j_out = j;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -190,6 +200,104 @@ __device__ __forceinline__ void rope_row16(uint32_t in[8], const Rope16 &r, int 
         const lk_bf16x2 b = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){y[0], y[1]}, lk_bf16x2);
         in[i] = __builtin_bit_cast(uint32_t, b);
     }
+}
+
+// ---- One row spread over a whole wave (the fused decode kernel's new key): lane l
+// holds features 2l and 2l + 1, feature-index bit 0 in registers and bits 1-6 as lane
+// bits 0-5.  Lanes exchange through VALU only (DPP and permlane swaps), so the row
+// costs one wave a few hundred cycles instead of a full 16-feature pass.  Every lane
+// of the wave must take part (full EXEC).
+
+// Value of lane (lane ^ kM), kM = 1 .. 32: DPP quad_perm for 1 and 2, row_shl:4 /
+// row_shr:4 for 4, row_ror:8 for 8 (within a 16-lane row, lane i + 8 mod 16 is i ^ 8),
+// v_permlane16_swap for 16 (it returns rows (0, 0, 2, 2) and (1, 1, 3, 3)), and
+// v_permlane32_swap for 32 (the low half twice, the high half twice).
+template <int kM>
+__device__ __forceinline__ uint32_t wave_xor_u32(uint32_t x) {
+    const int lane = __lane_id();
+    if constexpr (kM == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (kM == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (kM == 4) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x104, 0xF, 0xF, false);
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
+        return (lane & 4) ? dn : up;
+    } else if constexpr (kM == 8) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
+    } else if constexpr (kM == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? p[0] : p[1];
+    } else {
+        static_assert(kM == 32, "xor distance 1 .. 32");
+        const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? p[0] : p[1];
+    }
+}
+template <int kM>
+__device__ __forceinline__ double wave_xor_f64(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint64_t lo = wave_xor_u32<kM>((uint32_t)u), hi = wave_xor_u32<kM>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+template <int kM>
+__device__ __forceinline__ void wave_butterfly(double &x0, double &x1) {
+#pragma clang fp contract(off)
+    const bool upper = (__lane_id() & kM) != 0;
+    const double y0 = wave_xor_f64<kM>(x0), y1 = wave_xor_f64<kM>(x1);
+    x0 = upper ? (y0 - x0) : (x0 + y0);
+    x1 = upper ? (y1 - x1) : (x1 + y1);
+}
+
+// Returns this lane's two codes in bits 0-15 (feature 2l in the low byte) and the
+// row's exponent j (the same in every lane).  Arithmetic as quantize_row16.
+__device__ __forceinline__ uint32_t quantize_row_wave(uint32_t in, int &j_out) {
+#pragma clang fp contract(off)
+    double x0 = bf16_bits_to_double(in & 0xFFFFu), x1 = bf16_bits_to_double(in >> 16);
+    const double u = x0 + x1, v = x0 - x1;            // feature-index bit 0
+    x0 = u;
+    x1 = v;
+    wave_butterfly<1>(x0, x1);
+    wave_butterfly<2>(x0, x1);
+    wave_butterfly<4>(x0, x1);
+    wave_butterfly<8>(x0, x1);
+    wave_butterfly<16>(x0, x1);
+    wave_butterfly<32>(x0, x1);
+    x0 = scale_round(x0);
+    x1 = scale_round(x1);
+    double amax = __builtin_fmax(__builtin_fabs(x0), __builtin_fabs(x1));
+    amax = __builtin_fmax(amax, wave_xor_f64<1>(amax));
+    amax = __builtin_fmax(amax, wave_xor_f64<2>(amax));
+    amax = __builtin_fmax(amax, wave_xor_f64<4>(amax));
+    amax = __builtin_fmax(amax, wave_xor_f64<8>(amax));
+    amax = __builtin_fmax(amax, wave_xor_f64<16>(amax));
+    amax = __builtin_fmax(amax, wave_xor_f64<32>(amax));
+    const int j = scale_exponent(amax);
+    j_out = j;
+    lk_v2i16 w = {0, 0};
+    w = encode_e4m3_pair<false>(w, (float)__builtin_ldexp(x0, -j), (float)__builtin_ldexp(x1, -j));
+    return (uint32_t)(uint16_t)w[0];
+}
+
+// RoPE in the wave layout: feature i < 32 (lanes 0-15) pairs with i + 32 (lanes
+// 16-31, lane xor 16); c and s are this lane's two table entries, pairs
+// 2 (lane % 16) and 2 (lane % 16) + 1.  Same rounding as rope_row16.
+__device__ __forceinline__ void rope_row_wave(uint32_t &in, float2 c, float2 s) {
+#pragma clang fp contract(off)
+    const uint32_t partner = wave_xor_u32<16>(in);
+    const int lane = __lane_id();
+    if (lane >= 32) return;
+    const uint32_t flip = lane < 16 ? 0x80000000u : 0u;
+    const float cc[2] = {c.x, c.y}, ss[2] = {s.x, s.y};
+    float y[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const float own = __uint_as_float(((in >> (16 * h)) & 0xFFFFu) << 16);
+        const float oth = __uint_as_float(((partner >> (16 * h)) & 0xFFFFu) << 16);
+        y[h] = own * cc[h] + __uint_as_float(__float_as_uint(oth * ss[h]) ^ flip);
+    }
+    const lk_bf16x2 b = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){y[0], y[1]}, lk_bf16x2);
+    in = __builtin_bit_cast(uint32_t, b);
 }
 
 // Folded query weight of page "Index scores": fl32(fl32(w * 2^j) * fl32(128^-0.5)).

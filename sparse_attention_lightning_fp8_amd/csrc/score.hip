@@ -192,7 +192,9 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
 
     // Query, weights and (fused) new-key loads, issued before the K loads and never
     // under a branch, so the waits of the staging below count the K loads exactly.
-    uint4 qp0, qp1, kn0, kn1;
+    uint4 qp0, qp1;
+    uint32_t kn = 0;                                   // fused: new-key features 2 lane, 2 lane + 1
+    float2 krc = {0.f, 0.f}, krs = {0.f, 0.f};         // fused: their RoPE table entries
     float4 wv;
     float wr = 0.f;
     Rope32 rope_row;                                   // fused: the token's RoPE table row (scalar loads)
@@ -201,10 +203,16 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
         qp0 = qs[0];
         qp1 = qs[1];
         wr = a.w[(int64_t)qrow * LK_HEADS + head];
-        const uint4 *kns = reinterpret_cast<const uint4 *>(a.k_new + (int64_t)b * LK_DIM + 16 * sub);
-        kn0 = kns[0];
-        kn1 = kns[1];
-        if (a.rope_cos)                                // the step's token: shared by the query and the new key
+        kn = reinterpret_cast<const uint32_t *>(a.k_new + (int64_t)b * LK_DIM)[lane];
+        // The new key's table entries are loaded whether or not RoPE is on (a load
+        // under a branch would be waited for with all later loads); without tables
+        // they come from the key row itself and are ignored.
+        const bool rope_on = a.rope_cos != nullptr;
+        const float *kc_row = rope_on ? a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
+        const float *ks_row = rope_on ? a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
+        krc = reinterpret_cast<const float2 *>(kc_row)[lane & 15];
+        krs = reinterpret_cast<const float2 *>(ks_row)[lane & 15];
+        if (rope_on)                                   // the step's token: shared by the query and the new key
             load_rope32_uniform(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2),
                                 a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), rope_row);
     } else {
@@ -255,22 +263,18 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
             *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) = piece;
             if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = we;
         }
-        if (has_new && wave == 0) {                    // all 8 row groups of wave 0 compute the same key
-            uint32_t kin[8] = {kn0.x, kn0.y, kn0.z, kn0.w, kn1.x, kn1.y, kn1.z, kn1.w};
-            if (a.rope_cos) rope_row16(kin, rope, sub);
-            uint32_t kc[4];
+        if (has_new && wave == 0) {                    // the new key, spread over wave 0 (2 features a lane)
+            uint32_t kin = kn;
+            if (a.rope_cos) rope_row_wave(kin, krc, krs);
             int kj;
-            quantize_row16(kin, kc, kj);
-            if (lane < 8) {
-                const uint4 kpiece = make_uint4(kc[0], kc[1], kc[2], kc[3]);
-                const int64_t row = (int64_t)b * a.cache_seq_stride + pn;
-                *reinterpret_cast<uint4 *>(a.k_cache + row * LK_DIM + 16 * sub) = kpiece;
-                snew[sub] = kpiece;
-                if (sub == 0) {
-                    const float ksc = __builtin_ldexpf(1.0f, kj);
-                    a.k_scale[row] = ksc;
-                    snew_scale = ksc;
-                }
+            const uint32_t kc = quantize_row_wave(kin, kj);
+            const int64_t row = (int64_t)b * a.cache_seq_stride + pn;
+            reinterpret_cast<uint16_t *>(a.k_cache + row * LK_DIM)[lane] = (uint16_t)kc;
+            reinterpret_cast<uint16_t *>(snew)[lane] = (uint16_t)kc;
+            if (lane == 0) {
+                const float ksc = __builtin_ldexpf(1.0f, kj);
+                a.k_scale[row] = ksc;
+                snew_scale = ksc;
             }
         }
     } else {

@@ -90,3 +90,59 @@ def test_fused_ragged_edges():
     log("[fused] ragged edge rows")
     g = gpu_pipeline_fused(inp)
     _check_against_oracle(inp, g, list(range(wl.B)))
+
+
+def _new_key_rows(rows_bits: np.ndarray, rope: bool, seed: int):
+    """Write each row as the new key of its own one-slot sequence through
+    lk_decode_score; return the cache bytes and scales it wrote, and the oracle's."""
+    n = rows_bits.shape[0]
+    g = torch.Generator().manual_seed(seed)
+    dev = "cuda:0"
+    q = torch.randn(n, 64, 128, generator=g).to(torch.bfloat16).to(dev)
+    w = (torch.randn(n, 64, generator=g) * 0.125).to(dev)
+    k_new = torch.from_numpy(rows_bits.astype(np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+    cache = torch.full((n, 2, 128), 0xAA, dtype=torch.uint8, device=dev)
+    scale = torch.full((n, 2), -1.0, dtype=torch.float32, device=dev)
+    tabs = None
+    if rope:
+        ang = torch.rand(n, 32, generator=g, dtype=torch.float64) * 6.283185307179586
+        tabs = (torch.cos(ang).float(), torch.sin(ang).float())
+    api.lk_decode_score(q, w, k_new, cache, scale, T=1,
+                        rope=None if tabs is None else (tabs[0].to(dev), tabs[1].to(dev)))
+    torch.cuda.synchronize()
+    if tabs is None:
+        oc, os_ = O.quantize_rows(rows_bits)
+    else:
+        oc, os_ = O.rope_quantize_rows(rows_bits, tabs[0].numpy(), tabs[1].numpy())
+    return cache[:, 0].cpu().numpy(), scale[:, 0].cpu().numpy(), oc, os_
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_new_key_quantization_many_rows(rope):
+    """The new key is quantized by a whole wave (two features a lane); its bytes and
+    scale must equal the oracle's on random rows over 2^-20..2^20, on single-value
+    rows spanning the bf16 range, and on the edge rows of the quantizer tests.  With
+    RoPE the rows stay where the oracle's exact rotation holds (magnitudes within
+    2^38 after the rotation): the random rows and single values in [2^-60, 2^60]."""
+    g = torch.Generator().manual_seed(7)
+    rnd = torch.randn(3000, 128, generator=g) * torch.exp2(torch.randint(-20, 20, (3000, 1), generator=g).float())
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).float()
+    keep = (torch.isfinite(vals) & (vals.abs() < 2.0**120)).numpy()
+    if rope:
+        keep &= ((vals.abs() >= 2.0**-60) & (vals.abs() <= 2.0**60)).numpy()
+    single = np.zeros((int(keep.sum()) // 4 + 1, 128), np.uint16)
+    v = allbits[keep][::4]
+    single[:v.size, 5] = v
+    single[1::2, 77] = single[1::2, 5]
+    f = lambda a: W.bf16_bits(torch.tensor(a, dtype=torch.float32).to(torch.bfloat16))
+    edge = np.stack([f([0.0] * 128), f([-0.0] * 128), f([1.0] * 128), f([(-1.0) ** i for i in range(128)]),
+                     f([448.0 if i == 3 else 0.0 for i in range(128)]), f([2.0**-100] * 64 + [-(2.0**-100)] * 64),
+                     f([2.0**60 * (1 + i / 128) for i in range(128)]), f([2.0**-30 if i % 2 else 2.0**8 for i in range(128)]),
+                     f([float(i - 64) for i in range(128)]), f([2.0**-126, -(2.0**-133)] + [0.0] * 126)])
+    parts = [W.bf16_bits(rnd.to(torch.bfloat16)), single] + ([] if rope else [edge])
+    rows = np.concatenate(parts)
+    log(f"[fused] new-key quantization, {rows.shape[0]} rows, rope={rope}")
+    gc, gs, oc, os_ = _new_key_rows(rows, rope, seed=8)
+    bad = np.nonzero(np.any(gc != oc, axis=1) | (gs.view(np.uint32) != os_.view(np.uint32)))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[0]}: gpu {gc[bad[0]][:8]} {gs[bad[0]]} oracle {oc[bad[0]][:8]} {os_[bad[0]]}"
