@@ -243,10 +243,14 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
 
     // 2-3. Histogram of the bins (invalid elements count in hist[-1], a spare word),
     //      then the bin holding the k-th largest.
+    // The bins are kept (bin + 1 in 16-bit halves) for the classification below.
+    uint32_t bins[kPer / 2] = {};
 #pragma unroll
     for (int e = 0; e < kPer; e++) {
         if (!live(e >> 2)) continue;
-        atomicAdd(&hist[bin_of(e)], 1u);
+        const int bn = bin_of(e);
+        bins[e >> 1] |= (uint32_t)(bn + 1) << (16 * (e & 1));
+        atomicAdd(&hist[bn], 1u);
     }
     __syncthreads();
     select_bin(hist, (uint32_t)k, wsum, sel);
@@ -258,7 +262,7 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
 #pragma unroll
     for (int e = 0; e < kPer; e++) {
         if (!live(e >> 2)) continue;
-        const int bn = bin_of(e);                      // -1 (invalid) is never > or == cb
+        const int bn = (int)((bins[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) - 1;   // -1 (invalid) is never > or == cb
         gbits |= (bn > (int)cb ? 1u : 0u) << e;
         ebits |= (bn == (int)cb ? 1u : 0u) << e;
     }
