@@ -225,7 +225,9 @@ LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, in
  *   (per-split partial results), owned by the caller, contents need no initialisation.
  * Logits and the softmax run in fp32 on bf16 MFMA products; p is rounded to bf16 for
  * the weighted sum (fp32 accumulation).  Requires cache_rows <= cache_seq_stride; all
- * tensors 16-byte aligned except idx (4).  LK_E_SHAPE if the workspace is too small.
+ * tensors 16-byte aligned except idx (4).  LK_E_SHAPE if the workspace is too small;
+ * LK_E_UNSUPPORTED past the launch grid limits: B > 65535, or
+ * ceil(n_idx / 256) * B > 4194303 (one 512-thread block per 256 entries and 64 heads).
  */
 LK_API size_t lk_sparse_mla_workspace_size(int32_t B, int32_t n_idx);
 LK_API lk_status lk_sparse_mla_decode(const uint16_t *q_latent, const uint16_t *q_rope, const uint16_t *kv_latent,

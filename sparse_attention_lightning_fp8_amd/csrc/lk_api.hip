@@ -15,6 +15,7 @@ hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t
                                uint8_t *q_fp8_out, float *w_eff_out, const float *rope_cos,
                                const float *rope_sin, hipStream_t stream);
 size_t mla_workspace_bytes(int32_t B, int32_t n_idx);
+bool mla_grid_fits(int32_t B, int32_t n_idx);
 hipError_t launch_sparse_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *kv_lat,
                              const uint16_t *kv_rope, int64_t stride, int64_t cap, const int32_t *idx, int32_t B,
                              int32_t n_idx, float scale, float *out, void *workspace, hipStream_t stream);
@@ -236,7 +237,7 @@ LK_API lk_status lk_sparse_mla_decode(const uint16_t *q_latent, const uint16_t *
     if (!aligned(q_latent, 16) || !aligned(q_rope, 16) || !aligned(kv_latent, 16) || !aligned(kv_rope, 16) ||
         !aligned(out, 16) || !aligned(workspace, 16) || !aligned(idx, 4))
         return LK_E_UNSUPPORTED;
-    if (B > kMaxGridYZ) return LK_E_UNSUPPORTED;
+    if (B > kMaxGridYZ || !lk::mla_grid_fits(B, n_idx)) return LK_E_UNSUPPORTED;
     return from_hip(lk::launch_sparse_mla(q_latent, q_rope, kv_latent, kv_rope, cache_seq_stride, cache_rows, idx, B,
                                           n_idx, scale, out, workspace, stream));
 }

@@ -28,6 +28,10 @@
 //    lane l receives element l % 4 of the 8-byte pieces read by lanes 4i + l / 4).
 //    These reads run at about a quarter of the rate of 16-byte LDS reads (measured),
 //    so each B operand feeds both head tiles.  The P V waves also issue the DMAs.
+// The block's query (64 heads x 576 features, 72 KB) is moved once by DMA into chunk
+// buffers 2 and 3, which chunks 2 and 3 overwrite only after the score waves have read
+// it into registers: both waves of a pair need the same heads, and loading them from
+// global memory twice per block made the start of the kernel bandwidth-bound.
 // The split writes its unnormalised o with the running max m (base-2 logit units)
 // and sum l to the workspace.
 // Combine kernel: per (b, h), o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
@@ -115,6 +119,28 @@ __device__ __forceinline__ void gather_chunk(const MlaArgs &a, int b, const int3
     const int r = 8 * v + (lane >> 3);
     const int64_t row = rr < 0 ? 0 : rr;
     dma16(kr + row * kRopeRow + 16 * ((lane & 7) ^ (r & 7)), rope + 8 * v * kRopeRow);
+}
+
+// Query staging: head hh (0 .. 63) of the block goes to buffer 2 + hh / 32, row
+// r = hh % 32; latent 16-byte chunk j in slot j ^ lat_swizzle(r), rotary chunk j in
+// slot j ^ ((r / 2) % 8) (16 rows of a register read hit distinct banks).  Score wave w
+// moves heads 16w .. 16w+15: one DMA per latent row, one per eight rotary rows.
+__device__ __forceinline__ int qrope_swizzle(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ void stage_query(const MlaArgs &a, int b, int half, uint8_t (*lat)[kChunk * kLatRow],
+                                            uint8_t (*rope)[kChunk * kRopeRow], int w, int lane) {
+    const int64_t h0 = (int64_t)b * kH + half * kHeadsPerBlock;
+    const uint8_t *ql = reinterpret_cast<const uint8_t *>(a.q_lat) + h0 * kLatRow;
+    const uint8_t *qr = reinterpret_cast<const uint8_t *>(a.q_rope) + h0 * kRopeRow;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int hh = 16 * w + j, r = hh & 31;
+        dma16(ql + hh * kLatRow + 16 * (lane ^ lat_swizzle(r)), lat[2 + (hh >> 5)] + r * kLatRow);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int hh0 = 16 * w + 8 * i, hh = hh0 + (lane >> 3), r = hh & 31;
+        dma16(qr + hh * kRopeRow + 16 * ((lane & 7) ^ qrope_swizzle(r)), rope[2 + (hh0 >> 5)] + (hh0 & 31) * kRopeRow);
+    }
 }
 
 // Raise the running max only when a chunk exceeds it by more than 2^8 (base-2 logits):
@@ -275,26 +301,20 @@ struct SplitCtx {
 };
 
 // Barrier sequence, identical in both roles: slot list filled (the score waves' query
-// loads overlap it), chunks 0 and 1 issued with chunk 0 landed, then two per iteration
-// c = 0 .. nch (after the chunk maxima, after chunk c + 1 has landed), and one before
-// the sums are combined.  Iteration c scores chunk c and multiplies chunk c - 1; the
-// DMA of chunk c + 2 goes into the buffer of chunk c - 2, free since iteration c - 1.
-// Only the P V waves issue DMAs, and they issue no other global loads, so vmcnt counts
-// exactly their DMAs.
+// DMAs are in flight), chunks 0 and 1 issued with chunk 0 and the query landed, then
+// two per iteration c = 0 .. nch (after the chunk maxima, after chunk c + 1 has
+// landed), and one before the sums are combined.  Iteration c scores chunk c and
+// multiplies chunk c - 1; the DMA of chunk c + 2 goes into the buffer of chunk c - 2,
+// free since iteration c - 1 (chunk 2's, into the query staging, waits for the chunk
+// maxima of iteration 0, when every score wave holds its query fragments).  The P V
+// waves issue no global loads but their DMAs, so vmcnt counts exactly those.
 
 __device__ __forceinline__ void score_role(const MlaArgs &a, SharedMem &sm, const SplitCtx &x) {
     const int r16 = x.lane & 15, g4 = x.lane >> 4;
     ScoreState ss;
-    // Query fragments: A operand of head tile t, K-step k (features 32k .. 32k+31; k >= 16: rotary).
+    stage_query(a, x.b, x.half, sm.lat, sm.rope, x.wave, x.lane);
 #pragma unroll
     for (int t = 0; t < 2; t++) {
-        const int64_t h = (int64_t)x.b * kH + x.hbase + 16 * t + r16;
-        const uint16_t *ql = a.q_lat + h * kDc;
-        const uint16_t *qr = a.q_rope + h * kDr;
-#pragma unroll
-        for (int k = 0; k < 16; k++) ss.qa[t][k] = as_bf16x8(*reinterpret_cast<const uint4 *>(ql + 32 * k + 8 * g4));
-#pragma unroll
-        for (int k = 0; k < 2; k++) ss.qa[t][16 + k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qr + 32 * k + 8 * g4));
         ss.m[t] = -__builtin_inff();
         ss.l[t] = 0.f;
     }
@@ -302,8 +322,24 @@ __device__ __forceinline__ void score_role(const MlaArgs &a, SharedMem &sm, cons
     for (int kk = 0; kk < 4; kk++) ss.off_lat[kk] = r16 * kLatRow + 16 * ((4 * kk + g4) ^ lat_swizzle(r16));
 #pragma unroll
     for (int kk = 0; kk < 2; kk++) ss.off_rope[kk] = r16 * kRopeRow + 16 * ((4 * kk + g4) ^ (r16 & 7));
-    __syncthreads();                                           // slot list (and the query is loaded)
-    __syncthreads();                                           // chunk 0 in LDS
+    __syncthreads();                                           // slot list
+    __builtin_amdgcn_s_waitcnt(0x3F70);                        // vmcnt(0): this wave's query DMAs
+    __syncthreads();                                           // chunk 0 and the query in LDS
+    // Query fragments: A operand of head tile t, K-step k (features 32k .. 32k+31;
+    // k >= 16: rotary), head 32 grp + 16t + r16 = staging row 16t + r16 of buffer 2 + grp.
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        const int r = 16 * t + r16;
+        const uint8_t *ql = sm.lat[2 + x.grp] + r * kLatRow;
+        const uint8_t *qr = sm.rope[2 + x.grp] + r * kRopeRow;
+#pragma unroll
+        for (int k = 0; k < 16; k++)
+            ss.qa[t][k] = as_bf16x8(*reinterpret_cast<const uint4 *>(ql + 16 * ((4 * k + g4) ^ lat_swizzle(r))));
+#pragma unroll
+        for (int k = 0; k < 2; k++)
+            ss.qa[t][16 + k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qr + 16 * ((4 * k + g4) ^ qrope_swizzle(r))));
+    }
+    __syncthreads();                                           // query in registers
     float xs[2][4];
     for (int c = 0; c <= x.nch; c++) {
         if (c < x.nch) score_chunk(ss, sm, c % kBufs, c, x.wave, x.lane, x.sl2, xs);
@@ -367,9 +403,11 @@ __device__ __forceinline__ void pv_role(const MlaArgs &a, SharedMem &sm, const S
     __builtin_amdgcn_s_waitcnt(0x3F70);                        // vmcnt(0): chunk 0
     if (x.nch > 1) gather_chunk(a, x.b, sm.sidx, 1, sm.lat[1], sm.rope[1], v, lane);
     __syncthreads();                                           // chunk 0 in LDS
+    __syncthreads();                                           // query in registers
+    if (x.nch > 2) gather_chunk(a, x.b, sm.sidx, 2, sm.lat[2], sm.rope[2], v, lane);
     for (int c = 0; c <= x.nch; c++) {
         const bool more = c + 2 < x.nch;
-        if (more) gather_chunk(a, x.b, sm.sidx, c + 2, sm.lat[(c + 2) % kBufs], sm.rope[(c + 2) % kBufs], v, lane);
+        if (more && c > 0) gather_chunk(a, x.b, sm.sidx, c + 2, sm.lat[(c + 2) % kBufs], sm.rope[(c + 2) % kBufs], v, lane);
         if (c >= 1) {
             pv_rescale(ps, sm, (c - 1) & 1, lane);
             pv_tiles(ps, sm, (c - 1) % kBufs, (c - 1) & 1, lane, 0);
@@ -392,12 +430,24 @@ __device__ __forceinline__ void pv_role(const MlaArgs &a, SharedMem &sm, const S
                 op[(int64_t)(32 * mt + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4)) * kDc + 32 * n] = ps.o[mt][n][i];
 }
 
+// Workgroups are dealt to the eight XCDs in turn (block i to XCD i % 8), and each XCD
+// has its own L2.  Renumbering so that XCD k runs the consecutive logical blocks
+// k n / 8 .. (k + 1) n / 8 - 1 keeps the blocks of one sequence, which read the same
+// query and key rows, on one L2.  Grids whose size is not a multiple of 8 keep the
+// hardware order.
+__device__ __forceinline__ int xcd_local_block() {
+    const int n = gridDim.x, i = blockIdx.x;
+    return (n & 7) ? i : (i & 7) * (n >> 3) + (i >> 3);
+}
+
+// Logical block (b, head half, split), split fastest.
 __global__ void __launch_bounds__(kThreads) mla_split_kernel(MlaArgs a) {
     __shared__ __attribute__((aligned(16))) SharedMem sm;
     SplitCtx x;
-    x.split = blockIdx.x;
-    x.half = blockIdx.y;
-    x.b = blockIdx.z;
+    const int id = xcd_local_block();
+    x.split = id % a.nsplit;
+    x.half = (id / a.nsplit) & 1;
+    x.b = id / (2 * a.nsplit);
     x.lane = __lane_id();
     x.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     x.grp = (x.wave & 3) >> 1;                                 // head group: heads 32 grp .. +31 of the block
@@ -410,11 +460,14 @@ __global__ void __launch_bounds__(kThreads) mla_split_kernel(MlaArgs a) {
     else pv_role(a, sm, x);
 }
 
-// One block per (b, two heads): 128 threads x 4 features per head.  Splits are taken
+// One block per (b, two heads), XCD-local like the split kernel so that the partial
+// results of a sequence are read on the L2 that wrote them: 128 threads x 4 features
+// per head.  Splits are taken
 // eight at a time with every load of the group issued together (out-of-range splits
 // read the last one and get weight 0), merged into a running max / sum.
 __global__ void __launch_bounds__(256) mla_combine_kernel(MlaArgs a) {
-    const int h = 2 * blockIdx.x + (threadIdx.x >> 7), b = blockIdx.y;
+    const int id = xcd_local_block();
+    const int h = 2 * (id % (kH / 2)) + (threadIdx.x >> 7), b = id / (kH / 2);
     const int f = 4 * (threadIdx.x & 127);
     float M = -__builtin_inff(), den = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -457,6 +510,12 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaArgs a) {
 
 }  // namespace
 
+// Both grids are one-dimensional; a dispatch counts at most 2^32 - 1 work-items per axis.
+bool mla_grid_fits(int32_t B, int32_t n_idx) {
+    const int64_t nsplit = (n_idx + kSplit - 1) / kSplit;
+    return nsplit * (kH / kHeadsPerBlock) * B * kThreads <= 0xFFFFFFFFLL && (int64_t)(kH / 2) * B * 256 <= 0xFFFFFFFFLL;
+}
+
 size_t mla_workspace_bytes(int32_t B, int32_t n_idx) {
     const int64_t nsplit = (n_idx + kSplit - 1) / kSplit;
     return (size_t)B * nsplit * kH * (kDc + 2) * sizeof(float);
@@ -481,11 +540,11 @@ hipError_t launch_sparse_mla(const uint16_t *q_lat, const uint16_t *q_rope, cons
     a.out = out;
     if (cap == 0) a.nsplit = 0;                               // no valid slot: every output row is zero
     if (a.nsplit > 0) {
-        hipError_t e = launch(mla_split_kernel, dim3((unsigned)a.nsplit, kH / kHeadsPerBlock, (unsigned)B),
+        hipError_t e = launch(mla_split_kernel, dim3((unsigned)(a.nsplit * (kH / kHeadsPerBlock) * B)),
                               dim3(kThreads), 0u, stream, a);
         if (e != hipSuccess) return e;
     }
-    return launch(mla_combine_kernel, dim3(kH / 2, (unsigned)B), dim3(256), 0u, stream, a);
+    return launch(mla_combine_kernel, dim3((unsigned)(kH / 2 * B)), dim3(256), 0u, stream, a);
 }
 
 }  // namespace lk

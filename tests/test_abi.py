@@ -157,6 +157,8 @@ def test_sparse_mla_validation(lib):
     assert f(A + 8, A, A, A, 16, 16, A, 1, 8, 0.1, A, A, ws, None) == E_UNSUP
     assert f(A, A, A, A, 16, 16, A + 2, 1, 8, 0.1, A, A, ws, None) == E_UNSUP
     assert f(A, A, A, A, 16, 16, A, 70000, 8, 0.1, A, A, 1 << 40, None) == E_UNSUP   # grid limit
+    assert f(A, A, A, A, 16, 16, A, 60000, 25600, 0.1, A, A, 1 << 45, None) == E_UNSUP   # 6e6 blocks
+    assert f(A, A, A, A, 16, 16, A, 60000, 256, 0.1, A, A, 0, None) == E_SHAPE   # fits the grid, checks go on
     assert f(None, None, None, None, 16, 16, None, 0, 8, 0.1, None, None, 0, None) == OK
 
 
