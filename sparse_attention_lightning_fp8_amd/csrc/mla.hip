@@ -14,13 +14,13 @@
 // through the source address.  Four chunk buffers rotate; chunk c + 2 is in flight
 // while chunk c is scored and chunk c - 1 is multiplied into o.
 // Eight waves, two per SIMD, in two roles:
-//  - score waves (0..3): wave (a, kh) holds the query of heads 32a .. 32a+31 (576
-//    features, bf16, 144 registers) and computes S^T = K Q^T with
-//    v_mfma_f32_16x16x32_bf16 for keys 16kh .. 16kh+15 of the chunk, so that each lane
-//    holds 4 keys of 2 heads and the per-head softmax bookkeeping runs twice per lane.
-//    The pair (a, 0), (a, 1) exchanges per-head chunk maxima through LDS, so both
-//    apply the same running max; each writes p (bf16) for its keys and keeps per-lane
-//    partial sums l, added up once at the end.
+//  - score waves (0..3): wave a holds the query of heads 16a .. 16a+15 (576 features,
+//    bf16, 72 registers) and computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 for
+//    all 32 keys of the chunk (two key tiles), so that each lane holds 8 keys of one
+//    head and the four lanes of a head settle its chunk max by two lane swaps: the
+//    softmax needs no other wave, and one barrier per chunk suffices.  Each wave
+//    writes p (bf16) for its heads and keeps per-lane partial sums l, added up once
+//    at the end.  The key rows are read from LDS by all four score waves.
 //  - P V waves (4..7): wave v accumulates o for all 64 heads and latent features
 //    128v .. 128v+127 (128 registers) with v_mfma_f32_32x32x16_bf16, A = p from LDS
 //    (two 32-head tiles), B = 8 consecutive keys of one feature per lane, read from the
@@ -153,84 +153,109 @@ struct SharedMem {
     uint8_t rope[kBufs][kChunk * kRopeRow];   // 16 KB
     uint16_t p[2][kHeadsPerBlock * kPPitch];  // p of the chunk last scored, bf16 [head][key]
     float alpha[2][kHeadsPerBlock];           // o rescale factor per head for that chunk
-    int32_t rescale[2][2];                    // any alpha != 1, per head group
-    float part[kHeadsPerBlock][8];            // per head: chunk maxima (later sums) of the 8 lane groups of a pair
+    int32_t rescale[2][4];                    // any alpha != 1, per score wave (16 heads)
     int32_t sidx[kSplit];
 };
 
-// ---- score wave: S^T = K Q^T for 16 keys x 32 heads, softmax bookkeeping
+// ---- score wave: S^T = K Q^T for 32 keys x 16 heads, softmax bookkeeping
 struct ScoreState {
-    bf16x8 qa[2][18];                         // [head tile][K-step]
+    bf16x8 qa[18];                            // B operand per K-step (features 32k .. 32k+31; k >= 16: rotary)
     uint32_t off_lat[4], off_rope[2];         // swizzled LDS offsets (see score_chunk)
-    float m[2], l[2];                         // head 16t + r16 of the group; l: this lane's 4 keys
+    float m, l;                               // head 16 wave + r16; l: this lane's keys only
 };
 
-// Lane (r16, g4) of score wave (a, kh) holds keys 16kh + 4g4 + i (i = 0..3) of heads
-// 16t + r16 (t = 0, 1) of group a.
-__device__ __forceinline__ void score_chunk(ScoreState &st, SharedMem &sm, int buf, int c, int wave, int lane,
-                                            float sl2, float x[2][4]) {
-    const int r16 = lane & 15, g4 = lane >> 4, kh = wave & 1, grp = wave >> 1;
-    const uint8_t *lat = sm.lat[buf] + kh * 16 * kLatRow;
-    const uint8_t *rope = sm.rope[buf] + kh * 16 * kRopeRow;
-    f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    // A operand of K-step k: key 16kh + r16, features 32k + 8 g4 .. +7; chunk 16 j + c'
-    // of a row lies 256 j bytes after chunk c' (the XOR only touches the low 4 bits).
-#pragma unroll
-    for (int k = 0; k < 18; k++) {
-        const uint8_t *p0 = k < 16 ? lat + st.off_lat[k % 4] + 256 * (k / 4) : rope + st.off_rope[k - 16];
-        const bf16x8 kb = as_bf16x8(*reinterpret_cast<const uint4 *>(p0));
-        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, st.qa[0][k], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, st.qa[1][k], s[1], 0, 0, 0);
-    }
-    const int4 ids = *reinterpret_cast<const int4 *>(&sm.sidx[c * kChunk + 16 * kh + 4 * g4]);
-    const bool ok[4] = {ids.x >= 0, ids.y >= 0, ids.z >= 0, ids.w >= 0};
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-        float lm = -__builtin_inff();
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            x[t][i] = ok[i] ? s[t][i] * sl2 : -__builtin_inff();
-            lm = fmaxf(lm, x[t][i]);
-        }
-        sm.part[32 * grp + 16 * t + r16][4 * kh + g4] = lm;
-    }
+// Lanes r16, r16 + 16, r16 + 32, r16 + 48 hold the same head: combine their values.
+__device__ __forceinline__ float max4_groups(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));          // groups (0, 1) and (2, 3)
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float sum4_groups(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-// After the pair's maxima are in LDS: running max, p, sums.
-__device__ __forceinline__ void softmax_chunk(ScoreState &st, SharedMem &sm, int pbuf, int wave, int lane,
-                                              const float x[2][4]) {
-    const int r16 = lane & 15, g4 = lane >> 4, kh = wave & 1, grp = wave >> 1;
-    bool any = false;
+// Scores and softmax of chunk c for score wave a: lane (r16, g4) holds keys
+// 16kt + 4g4 + i (kt = 0, 1; i = 0..3) of head 16a + r16, so a head's chunk max, its
+// running max and its p all stay within the wave.  Writes p (bf16) and alpha into
+// buffer pbuf for the P V waves.
+__device__ __forceinline__ void score_chunk(ScoreState &st, SharedMem &sm, int buf, int c, int pbuf, int wave,
+                                            int lane, float sl2) {
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const uint8_t *lat = sm.lat[buf];
+    const uint8_t *rope = sm.rope[buf];
+    // Two accumulators per key tile (even and odd K-steps): four independent chains
+    // of dependent products keep the matrix pipeline busy.
+    f32x4 s2[2][2] = {};
+    // A operand of K-step k, key tile kt: key 16kt + r16, features 32k + 8 g4 .. +7;
+    // chunk 16 j + c' of a row lies 256 j bytes after chunk c' (the XOR only touches
+    // the low 4 bits, and it depends on the row's low 4 bits only).  The reads run
+    // kAhead K-steps ahead of the products (the order is pinned: one score wave per
+    // SIMD has nothing else to hide the LDS latency behind).
+    constexpr int kAhead = 6;
+    bf16x8 kb[18][2];
+    auto read = [&](int k) {
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-        const int hb = 32 * grp + 16 * t + r16;                 // head within the block
-        const float4 c0 = *reinterpret_cast<const float4 *>(&sm.part[hb][0]);
-        const float4 c1 = *reinterpret_cast<const float4 *>(&sm.part[hb][4]);
-        const float cm = fmaxf(fmaxf(fmaxf(c0.x, c0.y), fmaxf(c0.z, c0.w)), fmaxf(fmaxf(c1.x, c1.y), fmaxf(c1.z, c1.w)));
-        float alpha = 1.f;
-        if (cm > st.m[t] + kLazyMax) {                          // also when m is -inf and cm is finite
-            alpha = __builtin_amdgcn_exp2f(st.m[t] - cm);       // 0 when m was -inf
-            st.m[t] = cm;
-            any = true;
+        for (int kt = 0; kt < 2; kt++) {
+            const uint8_t *p0 = k < 16 ? lat + kt * 16 * kLatRow + st.off_lat[k % 4] + 256 * (k / 4)
+                                       : rope + kt * 16 * kRopeRow + st.off_rope[k - 16];
+            kb[k][kt] = as_bf16x8(*reinterpret_cast<const uint4 *>(p0));
         }
-        // m is -inf only while every key so far is masked: then p = 2^(-inf) = 0
-        const float mref = st.m[t] == -__builtin_inff() ? 0.f : st.m[t];
-        uint32_t q[4];
-        float sum = 0.f;
+    };
+#pragma unroll
+    for (int k = 0; k < kAhead; k++) read(k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 18; k++) {
+        if (k + kAhead < 18) read(k + kAhead);
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+            s2[kt][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[k][kt], st.qa[k], s2[kt][k & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const f32x4 s[2] = {s2[0][0] + s2[0][1], s2[1][0] + s2[1][1]};
+    float x[2][4];
+    float cm = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+        const int4 ids = *reinterpret_cast<const int4 *>(&sm.sidx[c * kChunk + 16 * kt + 4 * g4]);
+        const bool ok[4] = {ids.x >= 0, ids.y >= 0, ids.z >= 0, ids.w >= 0};
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            q[i] = bf16_rne(__builtin_amdgcn_exp2f(x[t][i] - mref));
+            x[kt][i] = ok[i] ? s[kt][i] * sl2 : -__builtin_inff();
+            cm = fmaxf(cm, x[kt][i]);
+        }
+    }
+    cm = max4_groups(cm);                                       // chunk max of the head
+    float alpha = 1.f;
+    bool up = false;
+    if (cm > st.m + kLazyMax) {                                 // also when m is -inf and cm is finite
+        alpha = __builtin_amdgcn_exp2f(st.m - cm);              // 0 when m was -inf
+        st.m = cm;
+        up = true;
+    }
+    // m is -inf only while every key so far is masked: then p = 2^(-inf) = 0
+    const float mref = st.m == -__builtin_inff() ? 0.f : st.m;
+    const int hb = 16 * wave + r16;                             // head within the block
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+        uint32_t q[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            q[i] = bf16_rne(__builtin_amdgcn_exp2f(x[kt][i] - mref));
             sum += __uint_as_float(q[i] << 16);
         }
-        st.l[t] = st.l[t] * alpha + sum;
-        *reinterpret_cast<uint2 *>(&sm.p[pbuf][hb * kPPitch + 16 * kh + 4 * g4]) =
+        *reinterpret_cast<uint2 *>(&sm.p[pbuf][hb * kPPitch + 16 * kt + 4 * g4]) =
             make_uint2(q[0] | (q[1] << 16), q[2] | (q[3] << 16));
-        if (kh == 0 && g4 == 0) sm.alpha[pbuf][hb] = alpha;
     }
-    if (kh == 0) {
-        const bool wany = __any(any);
-        if (lane == 0) sm.rescale[pbuf][grp] = wany;
-    }
+    st.l = st.l * alpha + sum;
+    if (g4 == 0) sm.alpha[pbuf][hb] = alpha;
+    const bool wany = __any(up);
+    if (lane == 0) sm.rescale[pbuf][wave] = wany;
 }
 
 // ---- P V wave: o[64 heads][128 features] += P V
@@ -244,7 +269,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ void pv_rescale(PvState &st, const SharedMem &sm, int pbuf, int lane) {
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
-        if (!sm.rescale[pbuf][mt]) continue;
+        if (!(sm.rescale[pbuf][2 * mt] | sm.rescale[pbuf][2 * mt + 1])) continue;
         // register i of a tile holds head row 8 (i / 4) + 4 (lane / 32) + i % 4
         float al[16];
 #pragma unroll
@@ -262,62 +287,68 @@ __device__ __forceinline__ void pv_rescale(PvState &st, const SharedMem &sm, int
     }
 }
 
-// Feature tiles n0, n0 + 1 (32 features each) of chunk `buf` with p from `pbuf`.
-__device__ __forceinline__ void pv_tiles(PvState &st, const SharedMem &sm, int buf, int pbuf, int lane, int n0) {
+// o += P V for chunk `buf` with p from `pbuf`.  Every LDS read of the chunk (p for both
+// K-steps, 16 transposing reads) is issued before the rescale and the products, in
+// pinned order, so that one P V wave per SIMD waits for LDS once per chunk instead of
+// once per K-step and feature tile.
+__device__ __forceinline__ void pv_chunk(PvState &st, const SharedMem &sm, int buf, int pbuf, int lane) {
     const uint8_t *lat = sm.lat[buf];
+    // A: head 32 mt + lane % 32, keys 16 ks + 8 (lane / 32) .. +7
+    bf16x8 pa[2][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-        // A: head 32 mt + lane % 32, keys 16 ks + 8 (lane / 32) .. +7
-        bf16x8 pa[2];
+    for (int ks = 0; ks < 2; ks++)
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
-            pa[mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+            pa[ks][mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(
                 &sm.p[pbuf][(32 * mt + (lane & 31)) * kPPitch + 16 * ks + 8 * (lane >> 5)]));
+    v4i16 hv[2][4][2];
 #pragma unroll
-        for (int nn = 0; nn < 2; nn++) {
-            const int n = n0 + nn;
-            v4i16 hv[2];
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int n = 0; n < 4; n++)
 #pragma unroll
             for (int h = 0; h < 2; h++)
-                hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lptr_t)(lat + st.off[h][n] + ks * 16 * kLatRow));
-            const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                hv[ks][n][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16 *)(lptr_t)(lat + st.off[h][n] + ks * 16 * kLatRow));
+    __builtin_amdgcn_sched_barrier(0);
+    pv_rescale(st, sm, pbuf, lane);
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int n = 0; n < 4; n++) {
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[ks][n][0], hv[ks][n][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int mt = 0; mt < 2; mt++) {
                 f32x16 acc;
 #pragma unroll
                 for (int i = 0; i < 16; i++) acc[i] = st.o[mt][n][i];
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[mt], vb, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks][mt], vb, acc, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 16; i++) st.o[mt][n][i] = acc[i];
             }
         }
-    }
 }
 
 // Block-level context shared by both roles.
 struct SplitCtx {
-    int b, split, half, nch, nk, k0, wave, lane, grp, hbase;
+    int b, split, half, nch, nk, k0, wave, lane;
     float sl2;
 };
 
 // Barrier sequence, identical in both roles: slot list filled (the score waves' query
-// DMAs are in flight), chunks 0 and 1 issued with chunk 0 and the query landed, then
-// two per iteration c = 0 .. nch (after the chunk maxima, after chunk c + 1 has
-// landed), and one before the sums are combined.  Iteration c scores chunk c and
-// multiplies chunk c - 1; the DMA of chunk c + 2 goes into the buffer of chunk c - 2,
-// free since iteration c - 1 (chunk 2's, into the query staging, waits for the chunk
-// maxima of iteration 0, when every score wave holds its query fragments).  The P V
+// DMAs are in flight), chunks 0 and 1 issued with chunk 0 and the query landed, query
+// read into registers, then one per iteration c = 0 .. nch (p of chunk c written,
+// chunk c + 1 landed).  Iteration c scores chunk c and multiplies chunk c - 1; the DMA
+// of chunk c + 2 goes into the buffer of chunk c - 2, free since iteration c - 1
+// (chunk 2's, into the query staging, goes once the query is in registers).  The P V
 // waves issue no global loads but their DMAs, so vmcnt counts exactly those.
 
 __device__ __forceinline__ void score_role(const MlaArgs &a, SharedMem &sm, const SplitCtx &x) {
     const int r16 = x.lane & 15, g4 = x.lane >> 4;
     ScoreState ss;
     stage_query(a, x.b, x.half, sm.lat, sm.rope, x.wave, x.lane);
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-        ss.m[t] = -__builtin_inff();
-        ss.l[t] = 0.f;
-    }
+    ss.m = -__builtin_inff();
+    ss.l = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) ss.off_lat[kk] = r16 * kLatRow + 16 * ((4 * kk + g4) ^ lat_swizzle(r16));
 #pragma unroll
@@ -325,43 +356,29 @@ __device__ __forceinline__ void score_role(const MlaArgs &a, SharedMem &sm, cons
     __syncthreads();                                           // slot list
     __builtin_amdgcn_s_waitcnt(0x3F70);                        // vmcnt(0): this wave's query DMAs
     __syncthreads();                                           // chunk 0 and the query in LDS
-    // Query fragments: A operand of head tile t, K-step k (features 32k .. 32k+31;
-    // k >= 16: rotary), head 32 grp + 16t + r16 = staging row 16t + r16 of buffer 2 + grp.
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-        const int r = 16 * t + r16;
-        const uint8_t *ql = sm.lat[2 + x.grp] + r * kLatRow;
-        const uint8_t *qr = sm.rope[2 + x.grp] + r * kRopeRow;
+    // Query fragments of head 16 wave + r16, which this wave staged itself: row
+    // 16 (wave % 2) + r16 of buffer 2 + wave / 2.
+    {
+        const int r = 16 * (x.wave & 1) + r16;
+        const uint8_t *ql = sm.lat[2 + (x.wave >> 1)] + r * kLatRow;
+        const uint8_t *qr = sm.rope[2 + (x.wave >> 1)] + r * kRopeRow;
 #pragma unroll
         for (int k = 0; k < 16; k++)
-            ss.qa[t][k] = as_bf16x8(*reinterpret_cast<const uint4 *>(ql + 16 * ((4 * k + g4) ^ lat_swizzle(r))));
+            ss.qa[k] = as_bf16x8(*reinterpret_cast<const uint4 *>(ql + 16 * ((4 * k + g4) ^ lat_swizzle(r))));
 #pragma unroll
         for (int k = 0; k < 2; k++)
-            ss.qa[t][16 + k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qr + 16 * ((4 * k + g4) ^ qrope_swizzle(r))));
+            ss.qa[16 + k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qr + 16 * ((4 * k + g4) ^ qrope_swizzle(r))));
     }
     __syncthreads();                                           // query in registers
-    float xs[2][4];
     for (int c = 0; c <= x.nch; c++) {
-        if (c < x.nch) score_chunk(ss, sm, c % kBufs, c, x.wave, x.lane, x.sl2, xs);
-        __syncthreads();                                       // chunk maxima
-        if (c < x.nch) softmax_chunk(ss, sm, c & 1, x.wave, x.lane, xs);
-        __syncthreads();                                       // chunk c + 1 in LDS
+        if (c < x.nch) score_chunk(ss, sm, c % kBufs, c, c & 1, x.wave, x.lane, x.sl2);
+        __syncthreads();                                       // p of chunk c, chunk c + 1 in LDS
     }
-    // sums: every lane group of the pair leaves its partial l in LDS; wave (a, 0)
-    // adds them up and writes m and l
-#pragma unroll
-    for (int t = 0; t < 2; t++) sm.part[32 * x.grp + 16 * t + r16][4 * (x.wave & 1) + g4] = ss.l[t];
-    __syncthreads();
-    if (!(x.wave & 1) && g4 == 0) {
-        float *mp = a.ml_part + (((int64_t)x.b * a.nsplit + x.split) * kH + x.hbase) * 2;
-#pragma unroll
-        for (int t = 0; t < 2; t++) {
-            const int hh = 16 * t + r16;
-            const float4 c0 = *reinterpret_cast<const float4 *>(&sm.part[32 * x.grp + hh][0]);
-            const float4 c1 = *reinterpret_cast<const float4 *>(&sm.part[32 * x.grp + hh][4]);
-            mp[2 * hh] = ss.m[t];
-            mp[2 * hh + 1] = ((c0.x + c0.y) + (c0.z + c0.w)) + ((c1.x + c1.y) + (c1.z + c1.w));
-        }
+    const float l = sum4_groups(ss.l);
+    if (g4 == 0) {
+        float *mp = a.ml_part + (((int64_t)x.b * a.nsplit + x.split) * kH + x.half * kHeadsPerBlock + 16 * x.wave + r16) * 2;
+        mp[0] = ss.m;
+        mp[1] = l;
     }
 }
 
@@ -409,16 +426,12 @@ __device__ __forceinline__ void pv_role(const MlaArgs &a, SharedMem &sm, const S
         const bool more = c + 2 < x.nch;
         if (more && c > 0) gather_chunk(a, x.b, sm.sidx, c + 2, sm.lat[(c + 2) % kBufs], sm.rope[(c + 2) % kBufs], v, lane);
         if (c >= 1) {
-            pv_rescale(ps, sm, (c - 1) & 1, lane);
-            pv_tiles(ps, sm, (c - 1) % kBufs, (c - 1) & 1, lane, 0);
+            pv_chunk(ps, sm, (c - 1) % kBufs, (c - 1) & 1, lane);
         }
-        __syncthreads();                                       // chunk maxima
-        if (c >= 1) pv_tiles(ps, sm, (c - 1) % kBufs, (c - 1) & 1, lane, 2);
         if (more) __builtin_amdgcn_s_waitcnt(0x3F70 | kDma);   // chunk c + 1 (all but c + 2's DMAs)
         else __builtin_amdgcn_s_waitcnt(0x3F70);
-        __syncthreads();                                       // chunk c + 1 in LDS
+        __syncthreads();                                       // p of chunk c, chunk c + 1 in LDS
     }
-    __syncthreads();
     // register i of a tile holds head row 8 (i / 4) + 4 (lane / 32) + i % 4, feature lane % 32
     float *op = a.o_part + (((int64_t)x.b * a.nsplit + x.split) * kH + x.half * kHeadsPerBlock) * kDc + 128 * v + (lane & 31);
 #pragma unroll
@@ -450,8 +463,6 @@ __global__ void __launch_bounds__(kThreads) mla_split_kernel(MlaArgs a) {
     x.b = id / (2 * a.nsplit);
     x.lane = __lane_id();
     x.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    x.grp = (x.wave & 3) >> 1;                                 // head group: heads 32 grp .. +31 of the block
-    x.hbase = x.half * kHeadsPerBlock + 32 * x.grp;
     x.sl2 = a.scale * 1.4426950408889634f;                     // logits in base-2 units
     x.k0 = x.split * kSplit;
     x.nk = min(kSplit, a.n_idx - x.k0);                        // >= 1 by the grid
