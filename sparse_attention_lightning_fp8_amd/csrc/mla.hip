@@ -75,10 +75,11 @@ typedef void __attribute__((address_space(3))) *lptr_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// bf16 (nearest-even) bits of a finite float.
-__device__ __forceinline__ uint32_t bf16_rne(float v) {
-    const uint32_t u = __float_as_uint(v);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// bf16 (nearest-even) bits of two floats, a in the low half: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // One 16-byte-per-lane DMA from global memory into LDS at lds + 16 * lane.  Written as
@@ -243,14 +244,15 @@ __device__ __forceinline__ void score_chunk(ScoreState &st, SharedMem &sm, int b
     float sum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; kt++) {
-        uint32_t q[4];
+        float e[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            q[i] = bf16_rne(__builtin_amdgcn_exp2f(x[kt][i] - mref));
-            sum += __uint_as_float(q[i] << 16);
-        }
-        *reinterpret_cast<uint2 *>(&sm.p[pbuf][hb * kPPitch + 16 * kt + 4 * g4]) =
-            make_uint2(q[0] | (q[1] << 16), q[2] | (q[3] << 16));
+        for (int i = 0; i < 4; i++) e[i] = __builtin_amdgcn_exp2f(x[kt][i] - mref);
+        const uint32_t w01 = bf16_pair(e[0], e[1]), w23 = bf16_pair(e[2], e[3]);
+        sum += __uint_as_float(w01 << 16);
+        sum += __uint_as_float(w01 & 0xFFFF0000u);
+        sum += __uint_as_float(w23 << 16);
+        sum += __uint_as_float(w23 & 0xFFFF0000u);
+        *reinterpret_cast<uint2 *>(&sm.p[pbuf][hb * kPPitch + 16 * kt + 4 * g4]) = make_uint2(w01, w23);
     }
     st.l = st.l * alpha + sum;
     if (g4 == 0) sm.alpha[pbuf][hb] = alpha;
