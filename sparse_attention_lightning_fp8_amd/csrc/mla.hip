@@ -235,8 +235,10 @@ __device__ __forceinline__ void score_chunk(ScoreState &st, SharedMem &sm, int b
     bool up = false;
     if (cm > st.m + kLazyMax) {                                 // also when m is -inf and cm is finite
         alpha = __builtin_amdgcn_exp2f(st.m - cm);              // 0 when m was -inf
+        // While m is -inf every p so far is 0, so o is still 0: no rescale is needed
+        // (this spares the P V waves a pass over o after the first chunk).
+        up = st.m != -__builtin_inff();
         st.m = cm;
-        up = true;
     }
     // m is -inf only while every key so far is masked: then p = 2^(-inf) = 0
     const float mref = st.m == -__builtin_inff() ? 0.f : st.m;
@@ -268,33 +270,28 @@ struct PvState {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ void pv_rescale(PvState &st, const SharedMem &sm, int pbuf, int lane) {
+// o = alpha o + P V for chunk `buf` with p and alpha from `pbuf`.  The rescale flags
+// (and alpha, where a head group needs it) are read first; every other LDS read of the
+// chunk (p for both K-steps, 16 transposing reads) is issued next, in pinned order, so
+// that the rescale and the first products wait only for the reads they use.
+__device__ __forceinline__ void pv_chunk(PvState &st, const SharedMem &sm, int buf, int pbuf, int lane) {
+    const uint8_t *lat = sm.lat[buf];
+    const int4 fl = *reinterpret_cast<const int4 *>(&sm.rescale[pbuf][0]);
+    const bool res[2] = {(fl.x | fl.y) != 0, (fl.z | fl.w) != 0};   // head tile mt = score waves 2mt, 2mt + 1
+    // register i of a tile holds head row 8 (i / 4) + 4 (lane / 32) + i % 4
+    float al[2][16];
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
-        if (!(sm.rescale[pbuf][2 * mt] | sm.rescale[pbuf][2 * mt + 1])) continue;
-        // register i of a tile holds head row 8 (i / 4) + 4 (lane / 32) + i % 4
-        float al[16];
+        if (!res[mt]) continue;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const float4 v = *reinterpret_cast<const float4 *>(&sm.alpha[pbuf][32 * mt + 8 * j + 4 * (lane >> 5)]);
-            al[4 * j] = v.x;
-            al[4 * j + 1] = v.y;
-            al[4 * j + 2] = v.z;
-            al[4 * j + 3] = v.w;
+            al[mt][4 * j] = v.x;
+            al[mt][4 * j + 1] = v.y;
+            al[mt][4 * j + 2] = v.z;
+            al[mt][4 * j + 3] = v.w;
         }
-#pragma unroll
-        for (int n = 0; n < 4; n++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) st.o[mt][n][i] *= al[i];
     }
-}
-
-// o += P V for chunk `buf` with p from `pbuf`.  Every LDS read of the chunk (p for both
-// K-steps, 16 transposing reads) is issued before the rescale and the products, in
-// pinned order, so that one P V wave per SIMD waits for LDS once per chunk instead of
-// once per K-step and feature tile.
-__device__ __forceinline__ void pv_chunk(PvState &st, const SharedMem &sm, int buf, int pbuf, int lane) {
-    const uint8_t *lat = sm.lat[buf];
     // A: head 32 mt + lane % 32, keys 16 ks + 8 (lane / 32) .. +7
     bf16x8 pa[2][2];
 #pragma unroll
@@ -313,7 +310,14 @@ __device__ __forceinline__ void pv_chunk(PvState &st, const SharedMem &sm, int b
                 hv[ks][n][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_v4i16 *)(lptr_t)(lat + st.off[h][n] + ks * 16 * kLatRow));
     __builtin_amdgcn_sched_barrier(0);
-    pv_rescale(st, sm, pbuf, lane);
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) {
+        if (!res[mt]) continue;
+#pragma unroll
+        for (int n = 0; n < 4; n++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) st.o[mt][n][i] *= al[mt][i];
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ks++)
 #pragma unroll
