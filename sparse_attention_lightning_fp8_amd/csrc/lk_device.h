@@ -56,6 +56,25 @@ __device__ __forceinline__ half8 fp8x8_to_half8(uint32_t a, uint32_t b) {
     return r;
 }
 
+// ---- LDS DMA (global_load_lds_*): lane l moves 4 or 16 bytes from its own global
+// address src into LDS at lds + 4 l or lds + 16 l.  Written as inline asm so that the
+// compiler's automatic waits neither count these loads nor make LDS reads wait for
+// them (it cannot tell LDS buffers apart); callers wait with s_waitcnt vmcnt before
+// reading what they moved.  The LDS base is an input bound to M0, which the compiler
+// writes; a DMA needs one wait state after M0 is written, hence the s_nop.
+typedef void __attribute__((address_space(3))) *lds_ptr_t;
+__device__ __forceinline__ void dma_b128(const void *src, const void *lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
+}
+__device__ __forceinline__ void dma_b32(const void *src, const void *lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(base) : "memory");
+}
+// s_waitcnt immediate that waits until at most n vector memory operations of this wave
+// are in flight (vmcnt is 6 bits on gfx950; expcnt and lgkmcnt are left alone).
+constexpr int vmcnt_imm(int n) { return 0x3F70 | (n & 15) | ((n >> 4) << 14); }
+
 // Sum across the two 32-lane halves of a wave for two values at once:
 // returns, in lanes 0-31, x[l] + x[l+32], and in lanes 32-63, y[l-32] + y[l].
 __device__ __forceinline__ float halves_sum_pair(float x, float y) {

@@ -82,15 +82,6 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// One 16-byte-per-lane DMA from global memory into LDS at lds + 16 * lane.  Written as
-// inline asm so that the compiler does not make later LDS reads wait for it (it cannot
-// tell the chunk buffers apart); the caller waits with vmcnt before the barrier that
-// publishes the data.  The LDS base is an input bound to M0, which the compiler writes;
-// an LDS DMA needs one wait state after M0 is written, hence the s_nop.
-__device__ __forceinline__ void dma16(const void *src, const void *lds) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lptr_t)lds);
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
-}
 
 // XOR pattern of latent row r: r % 16 rotated right by one bit.  Reads of one chunk
 // position from 16 consecutive rows (the S operand, ds_read_b128) then hit 16 distinct
@@ -115,11 +106,11 @@ __device__ __forceinline__ void gather_chunk(const MlaArgs &a, int b, const int3
     for (int j = 0; j < 8; j++) {
         const int r = 8 * v + j;
         const int64_t row = rows[j] < 0 ? 0 : rows[j];
-        dma16(kl + row * kLatRow + 16 * (lane ^ lat_swizzle(r)), lat + r * kLatRow);
+        dma_b128(kl + row * kLatRow + 16 * (lane ^ lat_swizzle(r)), lat + r * kLatRow);
     }
     const int r = 8 * v + (lane >> 3);
     const int64_t row = rr < 0 ? 0 : rr;
-    dma16(kr + row * kRopeRow + 16 * ((lane & 7) ^ (r & 7)), rope + 8 * v * kRopeRow);
+    dma_b128(kr + row * kRopeRow + 16 * ((lane & 7) ^ (r & 7)), rope + 8 * v * kRopeRow);
 }
 
 // Query staging: head hh (0 .. 63) of the block goes to buffer 2 + hh / 32, row
@@ -135,12 +126,12 @@ __device__ __forceinline__ void stage_query(const MlaArgs &a, int b, int half, u
 #pragma unroll
     for (int j = 0; j < 16; j++) {
         const int hh = 16 * w + j, r = hh & 31;
-        dma16(ql + hh * kLatRow + 16 * (lane ^ lat_swizzle(r)), lat[2 + (hh >> 5)] + r * kLatRow);
+        dma_b128(ql + hh * kLatRow + 16 * (lane ^ lat_swizzle(r)), lat[2 + (hh >> 5)] + r * kLatRow);
     }
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int hh0 = 16 * w + 8 * i, hh = hh0 + (lane >> 3), r = hh & 31;
-        dma16(qr + hh * kRopeRow + 16 * ((lane & 7) ^ qrope_swizzle(r)), rope[2 + (hh0 >> 5)] + (hh0 & 31) * kRopeRow);
+        dma_b128(qr + hh * kRopeRow + 16 * ((lane & 7) ^ qrope_swizzle(r)), rope[2 + (hh0 >> 5)] + (hh0 & 31) * kRopeRow);
     }
 }
 
@@ -360,7 +351,7 @@ __device__ __forceinline__ void score_role(const MlaArgs &a, SharedMem &sm, cons
 #pragma unroll
     for (int kk = 0; kk < 2; kk++) ss.off_rope[kk] = r16 * kRopeRow + 16 * ((4 * kk + g4) ^ (r16 & 7));
     __syncthreads();                                           // slot list
-    __builtin_amdgcn_s_waitcnt(0x3F70);                        // vmcnt(0): this wave's query DMAs
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                  // this wave's query DMAs
     __syncthreads();                                           // chunk 0 and the query in LDS
     // Query fragments of head 16 wave + r16, which this wave staged itself: row
     // 16 (wave % 2) + r16 of buffer 2 + wave / 2.
@@ -423,7 +414,7 @@ __device__ __forceinline__ void pv_role(const MlaArgs &a, SharedMem &sm, const S
     }
     __syncthreads();                                           // slot list
     gather_chunk(a, x.b, sm.sidx, 0, sm.lat[0], sm.rope[0], v, lane);
-    __builtin_amdgcn_s_waitcnt(0x3F70);                        // vmcnt(0): chunk 0
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                  // chunk 0
     if (x.nch > 1) gather_chunk(a, x.b, sm.sidx, 1, sm.lat[1], sm.rope[1], v, lane);
     __syncthreads();                                           // chunk 0 in LDS
     __syncthreads();                                           // query in registers
@@ -434,8 +425,8 @@ __device__ __forceinline__ void pv_role(const MlaArgs &a, SharedMem &sm, const S
         if (c >= 1) {
             pv_chunk(ps, sm, (c - 1) % kBufs, (c - 1) & 1, lane);
         }
-        if (more) __builtin_amdgcn_s_waitcnt(0x3F70 | kDma);   // chunk c + 1 (all but c + 2's DMAs)
-        else __builtin_amdgcn_s_waitcnt(0x3F70);
+        if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDma)); // chunk c + 1 (all but c + 2's DMAs)
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();                                       // p of chunk c, chunk c + 1 in LDS
     }
     // register i of a tile holds head row 8 (i / 4) + 4 (lane / 32) + i % 4, feature lane % 32
