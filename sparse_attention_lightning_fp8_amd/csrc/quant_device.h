@@ -52,6 +52,32 @@ __device__ __forceinline__ double scale_round(double r) {
     return round_to_bf16((r == 0.0 ? 0.0 : r) * kRotScale);
 }
 
+// The rounding of scale_round in two steps, for the callers that round many values:
+// p = (r + 0) * C64 (adding +0 turns an exact -0 sum into +0 and keeps every other
+// value), then, where p is zero or at least 2^-126 (a normal bf16 magnitude), nearest
+// even to 8 significant bits straight on the fp64 bits: add half an ulp at bit 45
+// (less one, plus the kept lowest bit) and clear bits 0-44.  That is round_to_bf16 for
+// those values, a carry into the exponent included.  Callers fall back to
+// round_to_bf16 when any p of theirs is a nonzero below 2^-126 (bf16 subnormals).
+__device__ __forceinline__ double scale_p(double r) {
+#pragma clang fp contract(off)
+    return (r + 0.0) * kRotScale;
+}
+__device__ __forceinline__ bool bf16_subnormal_range(double p) { return __builtin_fabs(p) < 0x1p-126 && p != 0.0; }
+__device__ __forceinline__ double round_to_bf16_normal(double p) {
+    uint64_t u = (uint64_t)__double_as_longlong(p);
+    u += 0xFFFFFFFFFFFull + ((u >> 45) & 1u);
+    u &= ~0x1FFFFFFFFFFFull;
+    return __longlong_as_double((long long)u);
+}
+
+// x with its sign flipped when neg.  A butterfly's upper lane computes y - x as
+// (-x) + y: IEEE subtraction is the addition of the negation, so the bits are those of
+// y - x, for one add instead of an add, a subtract and a select.
+__device__ __forceinline__ double neg_if(double x, bool neg) {
+    return __longlong_as_double(__double_as_longlong(x) ^ (neg ? (long long)0x8000000000000000ull : 0ll));
+}
+
 // Smallest j >= -126 with amax <= 448 * 2^j.  amax = f * 2^E with f in [0.5, 1):
 // j = E - 9 if f <= 0.875 (448 = 0.875 * 2^9), else E - 8.
 __device__ __forceinline__ int scale_exponent(double amax) {
@@ -93,17 +119,27 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
         const bool upper = (lane & m) != 0;
 #pragma unroll
         for (int e = 0; e < 16; e++) {
-            double y = __shfl_xor(x[e], m, 64);
-            x[e] = upper ? (y - x[e]) : (x[e] + y);
+            const double y = __shfl_xor(x[e], m, 64);
+            x[e] = neg_if(x[e], upper) + y;                 // upper: y - x; lower: x + y
         }
     }
-    // Scale, round to bf16, amax.
-    double amax = 0.0;
+    // Scale, round to bf16 (scale_round), amax.
+    bool sub = false;
 #pragma unroll
     for (int e = 0; e < 16; e++) {
-        x[e] = scale_round(x[e]);
-        amax = __builtin_fmax(amax, __builtin_fabs(x[e]));
+        x[e] = scale_p(x[e]);
+        sub |= bf16_subnormal_range(x[e]);
     }
+    if (__any(sub)) {
+#pragma unroll
+        for (int e = 0; e < 16; e++) x[e] = round_to_bf16(x[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; e++) x[e] = round_to_bf16_normal(x[e]);
+    }
+    double amax = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; e++) amax = __builtin_fmax(amax, __builtin_fabs(x[e]));
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) amax = __builtin_fmax(amax, __shfl_xor(amax, m, 64));
     const int j = scale_exponent(amax);
@@ -245,8 +281,8 @@ __device__ __forceinline__ void wave_butterfly(double &x0, double &x1) {
 #pragma clang fp contract(off)
     const bool upper = (__lane_id() & kM) != 0;
     const double y0 = wave_xor_f64<kM>(x0), y1 = wave_xor_f64<kM>(x1);
-    x0 = upper ? (y0 - x0) : (x0 + y0);
-    x1 = upper ? (y1 - x1) : (x1 + y1);
+    x0 = neg_if(x0, upper) + y0;                           // upper: y - x; lower: x + y
+    x1 = neg_if(x1, upper) + y1;
 }
 
 // Returns this lane's two codes in bits 0-15 (feature 2l in the low byte) and the
