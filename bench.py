@@ -55,6 +55,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-mla", action="store_true")
+    ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
@@ -388,6 +389,20 @@ def main():
              "separate_calls": {"step_us": uwall / args.steps * 1e6, "kernel_us": uper,
                                 "index_score_hbm_GBps": u_bytes / (uper["index_score"] * 1e-6) / 1e9,
                                 "index_score_algorithmic_bytes": u_bytes}}
+    if not args.no_ragged:
+        # ragged decode (64 rows, lengths uniform in [1024, 16384]) through the fused step
+        log("ragged_decode_b64: setting up")
+        torch.cuda.empty_cache()
+        rwl, rinp, rwall, rper = time_workload(api, "ragged_decode_b64", args.steps, args.warmup, 8, dev, fused=True)
+        rbytes = fused_decode_bytes(rwl, rinp)
+        rgbps = rbytes / (rper["decode_score"] * 1e-6) / 1e9
+        extra["ragged_decode_b64"] = {"step_us": rwall / args.steps * 1e6, "kernel_us": rper,
+                                      "algorithmic_bytes": rbytes, "decode_score_hbm_GBps": rgbps,
+                                      "decode_score_hbm_frac": rgbps / HBM_PEAK_GBPS,
+                                      "valid_keys": valid_pairs(rwl, rinp), "rotated_input_copies": 8}
+        log(f"ragged_decode_b64: decode_score {rper['decode_score']:.1f} us = {rgbps:.0f} GB/s")
+        del rinp
+        torch.cuda.empty_cache()
     if not args.no_prefill:
         for name in ("prefill_s4096", "chunked_prefill_b2_s4096"):
             log(f"{name}: setting up")

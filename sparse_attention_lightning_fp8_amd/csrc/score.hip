@@ -146,20 +146,29 @@ struct DecodeArgs {
     float *scores;              // [B, T]
 };
 
-template <bool kFused>
-__global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t sq[LK_HEADS * kQPitch];
-    __shared__ __attribute__((aligned(16))) float sw[LK_HEADS];
-    __shared__ __attribute__((aligned(16))) uint4 snew[8];   // fused: the new key's 128 codes
-    __shared__ float snew_scale;
+struct DecodeShared {
+    uint8_t sq[LK_HEADS * kQPitch];             // the row's quantized query (A operand source)
+    float sw[LK_HEADS];                         // its folded weights
+    uint4 snew[8];                              // fused: the new key's 128 codes
+    float snew_scale;
+};
+
+// Keys [blk0, blk0 + kDecKeysPerBlock) of score row qrow (one block's work item).
+// prep: bring in (fused: quantize) the row's query; otherwise sq and sw already hold
+// this row's query from the block's previous item.  `first`: the block's first item (a
+// later item that rewrites sq waits for every wave to be done with it).
+template <bool kFused, bool prep>
+__device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &sm, int qrow, int64_t blk0,
+                                            bool first) {
+    uint8_t *const sq = sm.sq;
+    float *const sw = sm.sw;
+    uint4 *const snew = sm.snew;
     const int lane = __lane_id();
     const int wave = threadIdx.x >> 6;
-    const int qrow = blockIdx.y;                       // b * S + t  (S == 1)
     const int b = qrow / a.rows.S;
     const int t = qrow - b * a.rows.S;
     const int64_t T = a.rows.T;
     const int64_t L = row_len(a.rows, b, t);
-    const int64_t blk0 = (int64_t)blockIdx.x * kDecKeysPerBlock;
     const int64_t key0 = blk0 + (int64_t)wave * kDecKeysPerWave;
     float *out = a.scores + (int64_t)qrow * T;
     const int head = threadIdx.x >> 3, sub = threadIdx.x & 7;   // fused: this thread's 16 features of a head
@@ -167,7 +176,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
         for (int64_t s = blk0 + threadIdx.x; s < blk0 + kDecKeysPerBlock && s < T; s += kDecThreads)
             out[s] = -__builtin_inff();
         if constexpr (kFused) {                        // a row with L == 0 still returns its quantized query
-            if (blockIdx.x == 0 && a.q_fp8_out) {
+            if (blk0 == 0 && a.q_fp8_out) {
                 const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
                 const uint4 q0 = qs[0], q1 = qs[1];
                 uint32_t in[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
@@ -190,8 +199,10 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
     const int64_t pn = L - 1;                          // fused: the new key's slot
     const bool has_new = kFused && pn < blk0 + kDecKeysPerBlock;
 
+    if (prep && !first) __syncthreads();               // every wave has its A fragments of the last row
     // Query, weights and (fused) new-key loads, issued before the K loads and never
     // under a branch, so the waits of the staging below count the K loads exactly.
+    // (An item that reuses the row's query still issues them; they are small.)
     uint4 qp0, qp1;
     uint32_t kn = 0;                                   // fused: new-key features 2 lane, 2 lane + 1
     float2 krc = {0.f, 0.f}, krs = {0.f, 0.f};         // fused: their RoPE table entries
@@ -246,6 +257,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
     // Keep these loads above this point, ahead of the staging and its waits.
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kFused) {
+      if (prep) {
         uint32_t in[8] = {qp0.x, qp0.y, qp0.z, qp0.w, qp1.x, qp1.y, qp1.z, qp1.w};
         Rope16 rope;
         if (a.rope_cos) {
@@ -259,10 +271,11 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
         *reinterpret_cast<uint4 *>(sq + head * kQPitch + 16 * sub) = piece;
         const float we = fold_weight(wr, j);
         if (sub == 0) sw[head] = we;
-        if (blockIdx.x == 0 && a.q_fp8_out) {
+        if (blk0 == 0 && a.q_fp8_out) {
             *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) = piece;
             if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = we;
         }
+      }
         if (has_new && wave == 0) {                    // the new key, spread over wave 0 (2 features a lane)
             uint32_t kin = kn;
             if (a.rope_cos) rope_row_wave(kin, krc, krs);
@@ -274,10 +287,10 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
             if (lane == 0) {
                 const float ksc = __builtin_ldexpf(1.0f, kj);
                 a.k_scale[row] = ksc;
-                snew_scale = ksc;
+                sm.snew_scale = ksc;
             }
         }
-    } else {
+    } else if (prep) {
         const int piece = threadIdx.x;                 // head piece / 8, 16-byte chunk piece % 8
         *reinterpret_cast<uint4 *>(sq + (piece >> 3) * kQPitch + 16 * (piece & 7)) = qp0;
         reinterpret_cast<float4 *>(sw)[lane & 15] = wv;    // duplicate stores of equal values
@@ -309,7 +322,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
                     for (int c = 0; c < 4; c++) kv[2 * p + h2][c] = snew[4 * hh + c];
                 }
             }
-            if (key0 + 64 * p + lane == pn) ks[p] = snew_scale;
+            if (key0 + 64 * p + lane == pn) ks[p] = sm.snew_scale;
         }
         const float p0 = score_tile(kv[2 * p], f);
         const float p1 = score_tile(kv[2 * p + 1], f);
@@ -317,6 +330,77 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
         const float sum = halves_sum_pair(p0, p1);
         const int64_t s = key0 + 64 * p + lane;
         if (s < T) out[s] = s < L ? sum * ks[p] : -__builtin_inff();
+    }
+}
+
+template <bool kFused>
+__global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) DecodeShared sm;
+    decode_item<kFused, true>(a, sm, blockIdx.y, (int64_t)blockIdx.x * kDecKeysPerBlock, true);
+}
+
+// Grids of more items than the chip runs at once (many rows, or ragged rows whose key
+// blocks mostly end early): a block per compute unit walks a contiguous range of the
+// valid items, in row order, so it quantizes each row's query once for all of its
+// items of that row, and items of different lengths even out across blocks.  Every
+// block derives the same schedule from the row lengths: row r has
+// ceil(L_r / kDecKeysPerBlock) items (one for a row with L_r = 0 when the quantized
+// query is requested), and the key blocks past them are swept to -inf by block r % grid.
+constexpr int kPersistMaxRows = kDecThreads;
+template <bool kFused>
+__global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) DecodeShared sm;
+    __shared__ int32_t first_item[kPersistMaxRows + 1];   // row r's items: first_item[r] .. first_item[r+1]-1
+    __shared__ int32_t wave_tot[kDecWaves];
+    const int nrows = a.rows.B * a.rows.S;             // <= kPersistMaxRows (host check)
+    const int64_t T = a.rows.T;
+    const int tid = threadIdx.x, lane = __lane_id(), wave = tid >> 6;
+    int nv = 0;
+    if (tid < nrows) {
+        const int64_t L = row_len(a.rows, tid / a.rows.S, tid % a.rows.S);
+        nv = (int)((L + kDecKeysPerBlock - 1) / kDecKeysPerBlock);
+        if (kFused && L == 0 && a.q_fp8_out) nv = 1;
+    }
+    // exclusive scan of nv over the rows (one per thread)
+    int incl = nv;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int base = 0;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; w++) base += w < wave ? wave_tot[w] : 0;
+    first_item[tid] = base + incl - nv;
+    if (tid == kDecThreads - 1) first_item[kDecThreads] = base + incl;
+    __syncthreads();
+    const int total = first_item[kDecThreads];
+    const int G = gridDim.x, g = blockIdx.x;
+    // -inf for the key blocks past each row's items
+    for (int r = g; r < nrows; r += G) {
+        const int64_t s0 = (int64_t)(first_item[r + 1] - first_item[r]) * kDecKeysPerBlock;
+        float *out = a.scores + (int64_t)r * T;
+        for (int64_t s = s0 + tid; s < T; s += kDecThreads) out[s] = -__builtin_inff();
+    }
+    const int i0 = (int)((int64_t)total * g / G), i1 = (int)((int64_t)total * (g + 1) / G);
+    int row = 0;
+    {                                                  // the row of item i0 (binary search)
+        int lo = 0, hi = nrows - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (first_item[mid] <= i0) lo = mid; else hi = mid - 1;
+        }
+        row = lo;
+    }
+    int prev = -1;
+    for (int it = i0; it < i1; it++) {
+        while (first_item[row + 1] <= it) row++;
+        const int64_t blk0 = (int64_t)(it - first_item[row]) * kDecKeysPerBlock;
+        if (row != prev) decode_item<kFused, true>(a, sm, row, blk0, it == i0);
+        else decode_item<kFused, false>(a, sm, row, blk0, false);
+        prev = row;
     }
 }
 
@@ -493,6 +577,35 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
     }
 }
 
+// Compute units of the current device (queried once per device).
+int cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Decode grid (S == 1): one block per (row, key block) when that fits the chip about
+// once; beyond, the persistent form with one block per compute unit.
+template <bool kFused>
+hipError_t launch_decode_grid(const DecodeArgs &a, hipStream_t stream) {
+    const RowsDev &rows = a.rows;
+    const int64_t nblk = (rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock;
+    const int64_t nrows = (int64_t)rows.B * rows.S;
+    const int cus = cu_count();
+    if (nrows <= kPersistMaxRows && nblk * nrows * 4 > (int64_t)cus * 5) {
+        const unsigned grid = (unsigned)(nblk * nrows < cus ? nblk * nrows : cus);
+        return launch(decode_persistent_kernel<kFused>, dim3(grid), dim3(kDecThreads), 0u, stream, a);
+    }
+    dim3 grid((unsigned)nblk, (unsigned)rows.B);
+    return launch(decode_kernel<kFused>, grid, dim3(kDecThreads), 0u, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
@@ -507,8 +620,7 @@ hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const ui
         a.cache_seq_stride = cache_seq_stride;
         a.rows = rows;
         a.scores = scores;
-        dim3 grid((unsigned)((rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock), (unsigned)rows.B);
-        return launch(decode_kernel<false>, grid, dim3(kDecThreads), 0u, stream, a);
+        return launch_decode_grid<false>(a, stream);
     } else {
         dim3 grid((unsigned)((rows.T + kPreSlice - 1) / kPreSlice), (unsigned)((rows.S + kPreWaves - 1) / kPreWaves),
                   (unsigned)rows.B);
@@ -536,8 +648,7 @@ hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t
     a.cache_seq_stride = cache_seq_stride;
     a.rows = rows;
     a.scores = scores;
-    dim3 grid((unsigned)((rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock), (unsigned)rows.B);
-    return launch(decode_kernel<true>, grid, dim3(kDecThreads), 0u, stream, a);
+    return launch_decode_grid<true>(a, stream);
 }
 
 }  // namespace lk

@@ -92,6 +92,29 @@ def test_fused_ragged_edges():
     _check_against_oracle(inp, g, list(range(wl.B)))
 
 
+@pytest.mark.gpu
+def test_fused_many_rows_edges():
+    """More row blocks than the chip holds at once (130 rows x 3 key blocks), so the
+    kernels run as one block per compute unit walking a range of the valid blocks; the
+    edge lengths repeat across rows so ranges start and end inside rows, rows with no
+    key still return their quantized query, and the fused and separate paths agree."""
+    edge = [0, 1, 2, 31, 32, 33, 1023, 1024, 1025, 2047, 2500, 2600, 1500]
+    lens = [edge[i % len(edge)] for i in range(130)]
+    wl = W.Workload(name="many_rows_edges", B=len(lens), S=1, T=2600, cap=2700, start_pos=-1, k=2048,
+                    causal=False, ragged=True)
+    base = W.make_inputs(wl, seed=5)
+    lt = torch.tensor(lens, dtype=torch.int32)
+    inp = W.Inputs(wl, base.q, base.k, base.w, lt, (lt - 1).to(torch.int32))
+    log("[fused] 130 rows x 3 key blocks, edge lengths")
+    g = gpu_pipeline_fused(inp)
+    rows = sorted(set(range(0, 13)) | {13, 40, 64, 77, 100, 116, 127, 128, 129})
+    _check_against_oracle(inp, g, rows)
+    # the standalone score kernel (same schedule) on the cache and query the fused step left
+    sc = api.lk_index_score(g.q_fp8, g.w_eff, g.cache, g.cache_scale, wl.T, seq_len=lt.to("cuda:0"))
+    torch.cuda.synchronize()
+    assert torch.equal(g.scores.view(torch.int32), sc.view(torch.int32)), "fused and standalone scores differ"
+
+
 def _new_key_rows(rows_bits: np.ndarray, rope: bool, seed: int):
     """Write each row as the new key of its own one-slot sequence through
     lk_decode_score; return the cache bytes and scales it wrote, and the oracle's."""
