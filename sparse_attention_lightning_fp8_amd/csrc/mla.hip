@@ -27,11 +27,11 @@
 //    key-major rows by two transposing LDS reads (ds_read_b64_tr_b16: within 16 lanes,
 //    lane l receives element l % 4 of the 8-byte pieces read by lanes 4i + l / 4).
 //    These reads run at about a quarter of the rate of 16-byte LDS reads (measured),
-//    so each B operand feeds both head tiles.  The P V waves also issue the DMAs.
-// The block's query (64 heads x 576 features, 72 KB) is moved once by DMA into chunk
-// buffers 2 and 3, which chunks 2 and 3 overwrite only after the score waves have read
-// it into registers: both waves of a pair need the same heads, and loading them from
-// global memory twice per block made the start of the kernel bandwidth-bound.
+//    so each B operand feeds both head tiles.  The P V waves also issue the chunk DMAs.
+// The block's query (64 heads x 576 features, 72 KB) goes by DMA into chunk buffers 2
+// and 3 (one instruction per 1 KB latent row), each score wave moving its own 16 heads,
+// and is read into registers before chunks 2 and 3 overwrite those buffers; the first
+// two chunks' gathers run meanwhile.
 // The split writes its unnormalised o with the running max m (base-2 logit units)
 // and sum l to the workspace.
 // Combine kernel: per (b, h), o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
