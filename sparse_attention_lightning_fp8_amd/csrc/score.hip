@@ -466,7 +466,9 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
     const int lane = __lane_id();
     const int wave = threadIdx.x >> 6;
     const int b = blockIdx.z;
-    const int t0 = blockIdx.y * kPreWaves;
+    // Row groups in reverse: under a causal mask the longest rows start first, so the
+    // heaviest blocks do not trail at the end of the launch.
+    const int t0 = (gridDim.y - 1 - blockIdx.y) * kPreWaves;
     const int64_t T = rows.T;
     const int64_t slice0 = (int64_t)blockIdx.x * kPreSlice;
     const int t = t0 + wave;

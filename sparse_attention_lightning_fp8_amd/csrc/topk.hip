@@ -10,17 +10,17 @@
 //
 // 1. A block reduction finds the row's smallest and largest valid score, lo and hi.
 // 2. Each element goes to one of 4096 equal-width bins of [lo, hi]:
-//    bin(v) = min(4095, trunc((v - lo) * (4096 / (hi - lo)))).  Rounded subtraction
-//    and multiplication by a positive constant are monotone, so v1 < v2 implies
-//    bin(v1) <= bin(v2): every element of a higher bin outranks every element of a
-//    lower one.  Unlike digits of the float's bits, equal-width bins spread the
-//    scores of a row evenly, so LDS histogram updates rarely collide and the bin
-//    that holds the k-th largest score holds few elements.
+//    bin(v) + 1 = trunc(fma(v - lo, 4095 * rcp(hi - lo), 1)), 1 .. 4096.  A rounded
+//    subtraction, a correctly rounded fma with a positive factor and truncation are
+//    each monotone, so v1 < v2 implies bin(v1) <= bin(v2): every element of a higher
+//    bin outranks every element of a lower one.  Unlike digits of the float's bits,
+//    equal-width bins spread the scores of a row evenly, so LDS histogram updates
+//    rarely collide and the bin that holds the k-th largest score holds few elements.
 // 3. A block scan of the histogram from the top finds that bin b and how many of
 //    its elements are still needed.
 // 4. Inside bin b the exact cut is found: if the bin is taken whole, nothing more;
-//    if it holds at most 64 elements, one wave ranks them pairwise (score
-//    descending, index ascending); otherwise a radix select walks the 32-bit
+//    if it holds at most 64 elements, they are ranked pairwise, 16 lanes per
+//    element (score descending, index ascending); otherwise a radix select walks the 32-bit
 //    order-preserving key of the bin's elements with digits of 12, 11 and 9 bits.
 //    A row whose range is empty or outside [1e-30, 1e30] puts every element in
 //    bin 0 and takes the radix path.
@@ -32,7 +32,8 @@
 //    the cut group; the cut group is one value except when a bin or digit is taken
 //    whole.
 //
-// Wave-level scans and reductions use DPP row shifts and row broadcasts.
+// Wave-level scans and reductions use DPP row shifts and row broadcasts; a reduction
+// over the 16 waves' partial results uses one DPP row.
 #include "lk_device.h"
 
 namespace lk {
@@ -71,35 +72,47 @@ __device__ __forceinline__ uint32_t row_scan16(uint32_t x) {
     return x;
 }
 
-// Running maximum and minimum over the lanes of a wave, ignoring NaN lanes (lanes
-// that DPP cannot source read NaN, which fmaxf/fminf ignore); lane 63 ends with the
-// wave's result.
-#define LK_DPP_F(x, ctrl, rm) __int_as_float(__builtin_amdgcn_update_dpp(0x7FC00000, __float_as_int(x), ctrl, rm, 0xf, false))
+// Running maximum and minimum over lanes with one DPP-routed v_max_f32 / v_min_f32 per
+// step.  A lane whose source is outside its row, or whose row is masked off, is not
+// written and keeps its value; a quiet-NaN operand yields the other operand (IEEE
+// mode), as fmaxf / fminf do.  The leading s_nop gives the DPP read of a VGPR written
+// by the previous VALU instruction its two wait states.
+#define LK_DPP_STEP(op, x, ctrl) asm("s_nop 1\n\t" op "_dpp %0, %0, %0 " ctrl : "+v"(x))
+// Lane 16r + 15 ends with the result over DPP row r.
+__device__ __forceinline__ float row_fmax16(float x) {
+    LK_DPP_STEP("v_max_f32", x, "row_shr:1 row_mask:0xf bank_mask:0xf");
+    LK_DPP_STEP("v_max_f32", x, "row_shr:2 row_mask:0xf bank_mask:0xf");
+    LK_DPP_STEP("v_max_f32", x, "row_shr:4 row_mask:0xf bank_mask:0xf");
+    LK_DPP_STEP("v_max_f32", x, "row_shr:8 row_mask:0xf bank_mask:0xf");
+    return x;
+}
+__device__ __forceinline__ float row_fmin16(float x) {
+    LK_DPP_STEP("v_min_f32", x, "row_shr:1 row_mask:0xf bank_mask:0xf");
+    LK_DPP_STEP("v_min_f32", x, "row_shr:2 row_mask:0xf bank_mask:0xf");
+    LK_DPP_STEP("v_min_f32", x, "row_shr:4 row_mask:0xf bank_mask:0xf");
+    LK_DPP_STEP("v_min_f32", x, "row_shr:8 row_mask:0xf bank_mask:0xf");
+    return x;
+}
+// Lane 63 ends with the result over the wave.
 __device__ __forceinline__ float wave_fmax(float x) {
-    x = fmaxf(x, LK_DPP_F(x, 0x111, 0xf));
-    x = fmaxf(x, LK_DPP_F(x, 0x112, 0xf));
-    x = fmaxf(x, LK_DPP_F(x, 0x114, 0xf));
-    x = fmaxf(x, LK_DPP_F(x, 0x118, 0xf));
-    x = fmaxf(x, LK_DPP_F(x, 0x142, 0xa));
-    x = fmaxf(x, LK_DPP_F(x, 0x143, 0xc));
+    x = row_fmax16(x);
+    LK_DPP_STEP("v_max_f32", x, "row_bcast:15 row_mask:0xa bank_mask:0xf");
+    LK_DPP_STEP("v_max_f32", x, "row_bcast:31 row_mask:0xc bank_mask:0xf");
     return x;
 }
 __device__ __forceinline__ float wave_fmin(float x) {
-    x = fminf(x, LK_DPP_F(x, 0x111, 0xf));
-    x = fminf(x, LK_DPP_F(x, 0x112, 0xf));
-    x = fminf(x, LK_DPP_F(x, 0x114, 0xf));
-    x = fminf(x, LK_DPP_F(x, 0x118, 0xf));
-    x = fminf(x, LK_DPP_F(x, 0x142, 0xa));
-    x = fminf(x, LK_DPP_F(x, 0x143, 0xc));
+    x = row_fmin16(x);
+    LK_DPP_STEP("v_min_f32", x, "row_bcast:15 row_mask:0xa bank_mask:0xf");
+    LK_DPP_STEP("v_min_f32", x, "row_bcast:31 row_mask:0xc bank_mask:0xf");
     return x;
 }
-#undef LK_DPP_F
+#undef LK_DPP_STEP
 
 // Sum of the per-wave totals of waves 0 .. wave-1 (before) and of all kWaves waves
 // (total), computed by every wave from the kWaves words of `part` (one per wave).
 __device__ __forceinline__ void wave_prefix(const uint32_t *part, int wave, uint32_t &before, uint32_t &total) {
     const int lane = __lane_id();
-    const uint32_t s = wave_scan(lane < kWaves ? part[lane] : 0u);
+    const uint32_t s = row_scan16(lane < kWaves ? part[lane] : 0u);   // DPP row 0 holds them all
     total = (uint32_t)__builtin_amdgcn_readlane((int)s, kWaves - 1);
     const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)s, (wave + kWaves - 1) & (kWaves - 1));
     before = wave > 0 ? b : 0u;
@@ -148,7 +161,7 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
     static_assert(kThreads * 4 == kBins && kThreads * kPer == LK_TOPK_MAX_T && kWaves == 16, "tiling");
     __shared__ __attribute__((aligned(16))) uint32_t hist_buf[4 + kBins];   // word 3: invalid elements
     uint32_t *const hist = hist_buf + 4;                                     // bins 0 .. kBins-1
-    __shared__ uint32_t wtot[4][kWaves];
+    __shared__ __attribute__((aligned(16))) uint32_t wtot[kWaves][4];
     __shared__ uint32_t wsum[kWaves];
     __shared__ float wred[2][kWaves];
     __shared__ uint32_t sel[3];
@@ -226,31 +239,42 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
         wred[1][wave] = mn;
     }
     __syncthreads();
-    // Every wave reduces the kWaves partial results itself (lane l reads wave l % 16).
-    mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_fmax(wred[0][lane & (kWaves - 1)])), 63));
-    mn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_fmin(wred[1][lane & (kWaves - 1)])), 63));
+    // Every wave reduces the kWaves partial results itself (lane l reads wave l % 16,
+    // so one DPP row holds all of them).
+    static_assert(kWaves == 16, "one DPP row per block reduction");
+    mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row_fmax16(wred[0][lane & (kWaves - 1)])), 15));
+    mn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row_fmin16(wred[1][lane & (kWaves - 1)])), 15));
     const float width = mx - mn;
     const bool spread = width >= 1e-30f && width <= 1e30f;
-    // scale = 4095 / width keeps (mx - mn) * scale below 4096 despite rounding, and
-    // every valid score of a spread row is finite, so bins are 0 .. 4095.
-    const float scale = 4095.f / width;
-    // Bin of element e, -1 for an invalid (NaN) element: fmaxf returns -1 for NaN.  A
-    // row without spread puts every valid element in bin 0.
-    auto bin_of = [&](int e) -> int {
-        if (spread) return (int)fmaxf((v[e] - mn) * scale, -1.0f);
-        return v[e] == v[e] ? 0 : -1;
-    };
+    // scale = 4095 * rcp(width), the hardware reciprocal (within 1 ulp), keeps
+    // fma(v - mn, scale, 1) below 4097, and every valid score of a spread row is finite,
+    // so bin + 1 is 1 .. 4096; it is monotone in v (a rounded subtraction, then a
+    // correctly rounded fma with a positive factor, then truncation).
+    const float scale = 4095.f * __builtin_amdgcn_rcpf(width);
 
     // 2-3. Histogram of the bins (invalid elements count in hist[-1], a spare word),
     //      then the bin holding the k-th largest.
-    // The bins are kept (bin + 1 in 16-bit halves) for the classification below.
+    // bin + 1 of every element is kept in 16-bit halves for the classification below;
+    // an invalid element (NaN) and every element of a dead group keep 0.  A wave whose
+    // elements are all valid takes a straight-line loop without those checks.
     uint32_t bins[kPer / 2] = {};
+    const bool wave_full = wave_rem >= 4 * kThreads * (kPer / 4 - 1) + 4 * 64;
+    if (spread && wave_full) {
 #pragma unroll
-    for (int e = 0; e < kPer; e++) {
-        if (!live(e >> 2)) continue;
-        const int bn = bin_of(e);
-        bins[e >> 1] |= (uint32_t)(bn + 1) << (16 * (e & 1));
-        atomicAdd(&hist[bn], 1u);
+        for (int e = 0; e < kPer; e++) {
+            const uint32_t b1 = (uint32_t)fmaf(v[e] - mn, scale, 1.0f);
+            bins[e >> 1] |= b1 << (16 * (e & 1));
+            atomicAdd(&hist[(int)b1 - 1], 1u);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kPer; e++) {
+            if (!live(e >> 2)) continue;
+            // fmaxf maps NaN to 0; a row without spread puts every valid element in bin 0.
+            const int b1 = spread ? (int)fmaxf(fmaf(v[e] - mn, scale, 1.0f), 0.0f) : (v[e] == v[e] ? 1 : 0);
+            bins[e >> 1] |= (uint32_t)b1 << (16 * (e & 1));
+            atomicAdd(&hist[b1 - 1], 1u);
+        }
     }
     __syncthreads();
     select_bin(hist, (uint32_t)k, wsum, sel);
@@ -258,13 +282,13 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
     uint32_t need = (uint32_t)k - sel[1];
 
     // 4. Classify: gbits = elements of higher bins (taken), ebits = elements of bin cb.
+    //    An invalid or dead element (bin + 1 == 0) is in neither.
     uint32_t gbits = 0, ebits = 0;
 #pragma unroll
     for (int e = 0; e < kPer; e++) {
-        if (!live(e >> 2)) continue;
-        const int bn = (int)((bins[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) - 1;   // -1 (invalid) is never > or == cb
-        gbits |= (bn > (int)cb ? 1u : 0u) << e;
-        ebits |= (bn == (int)cb ? 1u : 0u) << e;
+        const uint32_t b1 = (bins[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        gbits |= (b1 > cb + 1 ? 1u : 0u) << e;
+        ebits |= (b1 == cb + 1 ? 1u : 0u) << e;
     }
     // The cut inside bin cb: of its elements, those whose key & pmask exceeds prefix
     // join gbits, and the `need` lowest-index ones whose key & pmask equals prefix
@@ -352,37 +376,53 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
     }
     uint32_t incl[4];
 #pragma unroll
-    for (int f = 0; f < 4; f++) {
-        incl[f] = wave_scan(cnt4[f]);
-        if (lane == 63) wtot[f][wave] = incl[f];
-    }
+    for (int f = 0; f < 4; f++) incl[f] = wave_scan(cnt4[f]);
+    if (lane == 63) *reinterpret_cast<uint4 *>(wtot[wave]) = make_uint4(incl[0], incl[1], incl[2], incl[3]);
     __syncthreads();
+    // The four fields' sums over the lower waves and over all waves: lane l < 16 reads
+    // wave l's totals (DPP row 0 holds them all) and the four row scans run together.
+    uint32_t before[4], total[4];
+    {
+        const uint4 wt = lane < kWaves ? *reinterpret_cast<const uint4 *>(wtot[lane]) : make_uint4(0, 0, 0, 0);
+        const uint32_t sc[4] = {row_scan16(wt.x), row_scan16(wt.y), row_scan16(wt.z), row_scan16(wt.w)};
+#pragma unroll
+        for (int f = 0; f < 4; f++) {
+            total[f] = (uint32_t)__builtin_amdgcn_readlane((int)sc[f], kWaves - 1);
+            const uint32_t bf = (uint32_t)__builtin_amdgcn_readlane((int)sc[f], (wave + kWaves - 1) & (kWaves - 1));
+            before[f] = wave > 0 ? bf : 0u;
+        }
+    }
+    // Stores address the row by 32-bit byte offsets (positions kept times 4).  The upper
+    // group holds exactly n_gt elements (every element above the cut, counted by the
+    // selection), so its offsets stay below 4 n_gt; the clamp to the row only keeps a
+    // store in bounds should that ever fail.
+    char *const outb = reinterpret_cast<char *>(out);
+    const uint32_t row_end4 = 4u * (uint32_t)(k - 1);
     uint32_t gbase = 0, ebase = 0;
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-        uint32_t gb, gt, eb, et;
-        wave_prefix(wtot[h], wave, gb, gt);
-        wave_prefix(wtot[2 + h], wave, eb, et);
-        const uint32_t gx = incl[h] - cnt4[h] + gb, ex = incl[2 + h] - cnt4[2 + h] + eb;
+        const uint32_t gx = incl[h] - cnt4[h] + before[h], ex = incl[2 + h] - cnt4[2 + h] + before[2 + h];
 #pragma unroll
         for (int half = 0; half < 2; half++) {
             const int j = 2 * h + half;
+            const int32_t base = 4 * (tid + kThreads * j);
             uint32_t gm = (gbits >> (4 * j)) & 0xFu, em = (ebits >> (4 * j)) & 0xFu;
-            uint32_t gr = gbase + ((gx >> (16 * half)) & 0xFFFFu), er = ebase + ((ex >> (16 * half)) & 0xFFFFu);
+            uint32_t g4 = 4u * (gbase + ((gx >> (16 * half)) & 0xFFFFu));
+            uint32_t er = ebase + ((ex >> (16 * half)) & 0xFFFFu);
             while (gm) {
                 const int c = __builtin_ctz(gm);
                 gm &= gm - 1;
-                if (gr < n_gt) out[gr] = 4 * (tid + kThreads * j) + c;
-                gr++;
+                *reinterpret_cast<int32_t *>(outb + min(g4, row_end4)) = base + c;
+                g4 += 4u;
             }
             while (em) {
                 const int c = __builtin_ctz(em);
                 em &= em - 1;
-                if (er < need) out[n_gt + er] = 4 * (tid + kThreads * j) + c;
+                if (er < need) *reinterpret_cast<int32_t *>(outb + 4u * (n_gt + er)) = base + c;
                 er++;
             }
-            gbase += (gt >> (16 * half)) & 0xFFFFu;
-            ebase += (et >> (16 * half)) & 0xFFFFu;
+            gbase += (total[h] >> (16 * half)) & 0xFFFFu;
+            ebase += (total[2 + h] >> (16 * half)) & 0xFFFFu;
         }
     }
 }
