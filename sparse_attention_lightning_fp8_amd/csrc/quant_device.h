@@ -52,18 +52,11 @@ __device__ __forceinline__ double scale_round(double r) {
     return round_to_bf16((r == 0.0 ? 0.0 : r) * kRotScale);
 }
 
-// The rounding of scale_round in two steps, for the callers that round many values:
-// p = (r + 0) * C64 (adding +0 turns an exact -0 sum into +0 and keeps every other
-// value), then, where p is zero or at least 2^-126 (a normal bf16 magnitude), nearest
-// even to 8 significant bits straight on the fp64 bits: add half an ulp at bit 45
-// (less one, plus the kept lowest bit) and clear bits 0-44.  That is round_to_bf16 for
-// those values, a carry into the exponent included.  Callers fall back to
-// round_to_bf16 when any p of theirs is a nonzero below 2^-126 (bf16 subnormals).
-__device__ __forceinline__ double scale_p(double r) {
-#pragma clang fp contract(off)
-    return (r + 0.0) * kRotScale;
-}
-__device__ __forceinline__ bool bf16_subnormal_range(double p) { return __builtin_fabs(p) < 0x1p-126 && p != 0.0; }
+// Nearest even to 8 significant bits straight on the fp64 bits (add half an ulp at
+// bit 45, less one, plus the kept lowest bit, then clear bits 0-44): round_to_bf16 for
+// every p that is zero or at least 2^-126 in magnitude (a normal bf16 magnitude), a
+// carry into the exponent included.  Below 2^-126 it keeps more bits than bf16 has
+// there, and its magnitude stays at most 2^-126.
 __device__ __forceinline__ double round_to_bf16_normal(double p) {
     uint64_t u = (uint64_t)__double_as_longlong(p);
     u += 0xFFFFFFFFFFFull + ((u >> 45) & 1u);
@@ -71,11 +64,12 @@ __device__ __forceinline__ double round_to_bf16_normal(double p) {
     return __longlong_as_double((long long)u);
 }
 
-// x with its sign flipped when neg.  A butterfly's upper lane computes y - x as
-// (-x) + y: IEEE subtraction is the addition of the negation, so the bits are those of
-// y - x, for one add instead of an add, a subtract and a select.
-__device__ __forceinline__ double neg_if(double x, bool neg) {
-    return __longlong_as_double(__double_as_longlong(x) ^ (neg ? (long long)0x8000000000000000ull : 0ll));
+// One cross-lane butterfly output: y - x in the upper lane of a pair, x + y in the
+// lower, as fma(x, -1 or +1, y).  Multiplying by -1 is exact and the fma rounds once,
+// so the result has the bits of the subtraction or the addition (signed zeros
+// included), in one instruction.
+__device__ __forceinline__ double butterfly_out(double x, double sign, double y) {
+    return __builtin_fma(x, sign, y);
 }
 
 // Smallest j >= -126 with amax <= 448 * 2^j.  amax = f * 2^E with f in [0.5, 1):
@@ -116,32 +110,42 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
     const int lane = __lane_id();
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) {
-        const bool upper = (lane & m) != 0;
+        const double sign = (lane & m) ? -1.0 : 1.0;
 #pragma unroll
         for (int e = 0; e < 16; e++) {
             const double y = __shfl_xor(x[e], m, 64);
-            x[e] = neg_if(x[e], upper) + y;                 // upper: y - x; lower: x + y
+            x[e] = butterfly_out(x[e], sign, y);           // upper: y - x; lower: x + y
         }
     }
-    // Scale, round to bf16 (scale_round), amax.
-    bool sub = false;
+    // Scale and round to bf16 (scale_round), and the row's amax.  p = r * C64 keeps the
+    // sign of an exact zero sum; a -0 sum needs every input to be a zero (an exact
+    // cancellation of nonzero terms rounds to +0), so only an all-zero row can hold
+    // one, and its codes are set to +0 below.  (A nonzero p that rounds to zero keeps
+    // its sign.)
+    // The bit rounding is exact for every nonzero |p| >= 2^-126.  A nonzero p below
+    // that only matters when the scale exponent is -117 or less (otherwise both
+    // roundings, at most 2^-126 in magnitude, times 2^-j <= 2^-10, encode to a zero of
+    // p's sign), which needs amax <= 448 * 2^-117 < 2^-108; rows with a smaller amax
+    // (zero rows included) take the exact rounding.  Rounding is monotone and odd, so
+    // the row's amax is the rounding of max |p|.
+    double amax = 0.0;
 #pragma unroll
     for (int e = 0; e < 16; e++) {
-        x[e] = scale_p(x[e]);
-        sub |= bf16_subnormal_range(x[e]);
+        x[e] = x[e] * kRotScale;
+        amax = __builtin_fmax(amax, __builtin_fabs(x[e]));
     }
-    if (__any(sub)) {
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) amax = __builtin_fmax(amax, __shfl_xor(amax, m, 64));
+    const bool zero_row = amax == 0.0;                 // every input a zero (not: every p rounds to zero)
+    if (__any(amax < 0x1p-108)) {
 #pragma unroll
         for (int e = 0; e < 16; e++) x[e] = round_to_bf16(x[e]);
+        amax = round_to_bf16(amax);
     } else {
 #pragma unroll
         for (int e = 0; e < 16; e++) x[e] = round_to_bf16_normal(x[e]);
+        amax = round_to_bf16_normal(amax);
     }
-    double amax = 0.0;
-#pragma unroll
-    for (int e = 0; e < 16; e++) amax = __builtin_fmax(amax, __builtin_fabs(x[e]));
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) amax = __builtin_fmax(amax, __shfl_xor(amax, m, 64));
     const int j = scale_exponent(amax);
     j_out = j;
 #pragma unroll
@@ -152,7 +156,7 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
         lk_v2i16 w = {0, 0};
         w = encode_e4m3_pair<false>(w, q[0], q[1]);
         w = encode_e4m3_pair<true>(w, q[2], q[3]);
-        out[i] = __builtin_bit_cast(uint32_t, w);
+        out[i] = zero_row ? 0u : __builtin_bit_cast(uint32_t, w);   // an all-zero row: +0 codes
     }
 }
 
@@ -279,10 +283,10 @@ __device__ __forceinline__ double wave_xor_f64(double x) {
 template <int kM>
 __device__ __forceinline__ void wave_butterfly(double &x0, double &x1) {
 #pragma clang fp contract(off)
-    const bool upper = (__lane_id() & kM) != 0;
+    const double sign = (__lane_id() & kM) ? -1.0 : 1.0;
     const double y0 = wave_xor_f64<kM>(x0), y1 = wave_xor_f64<kM>(x1);
-    x0 = neg_if(x0, upper) + y0;                           // upper: y - x; lower: x + y
-    x1 = neg_if(x1, upper) + y1;
+    x0 = butterfly_out(x0, sign, y0);                      // upper: y - x; lower: x + y
+    x1 = butterfly_out(x1, sign, y1);
 }
 
 // Returns this lane's two codes in bits 0-15 (feature 2l in the low byte) and the
