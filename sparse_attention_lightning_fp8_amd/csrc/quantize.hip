@@ -44,6 +44,7 @@ __device__ __forceinline__ void key_row(const KeyJob &k, int64_t g, int sub) {
     const int64_t i = g - b * k.n_rows;
     const uint4 *src = reinterpret_cast<const uint4 *>(k.x + (b * k.x_seq_stride + i) * LK_DIM + sub * 16);
     uint4 v0 = src[0], v1 = src[1];
+    const int64_t p = (k.positions ? (int64_t)k.positions[b] : k.row_offset) + i;   // loaded with the row
     uint32_t in[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     if (k.rope_cos) {
         Rope16 r;
@@ -53,7 +54,6 @@ __device__ __forceinline__ void key_row(const KeyJob &k, int64_t g, int sub) {
     uint32_t out[4];
     int j;
     quantize_row16(in, out, j);
-    const int64_t p = (k.positions ? (int64_t)k.positions[b] : k.row_offset) + i;
     if (p < 0 || p >= k.cache_rows) return;
     const int64_t row = b * k.cache_seq_stride + p;
     *reinterpret_cast<uint4 *>(k.cache + row * LK_DIM + sub * 16) = make_uint4(out[0], out[1], out[2], out[3]);
@@ -63,6 +63,7 @@ __device__ __forceinline__ void key_row(const KeyJob &k, int64_t g, int sub) {
 __device__ __forceinline__ void query_row(const QueryJob &q, int64_t g, int sub) {
     const uint4 *src = reinterpret_cast<const uint4 *>(q.q + g * LK_DIM + sub * 16);
     uint4 v0 = src[0], v1 = src[1];
+    const float wg = q.w[g];                           // with the row's loads, not after the rotation
     uint32_t in[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     if (q.rope_cos) {
         const int64_t tok = g / q.heads;
@@ -75,7 +76,7 @@ __device__ __forceinline__ void query_row(const QueryJob &q, int64_t g, int sub)
     quantize_row16(in, out, j);
     *reinterpret_cast<uint4 *>(q.q_fp8 + g * LK_DIM + sub * 16) = make_uint4(out[0], out[1], out[2], out[3]);
     if (sub == 0) {
-        q.w_eff[g] = fold_weight(q.w[g], j);
+        q.w_eff[g] = fold_weight(wg, j);
         if (q.q_scale) q.q_scale[g] = __builtin_ldexpf(1.0f, j);
     }
 }
