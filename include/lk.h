@@ -53,7 +53,7 @@ typedef enum lk_status {
     LK_OK = 0,
     LK_E_NULL = -1,        /* a required pointer is NULL                               */
     LK_E_SHAPE = -2,       /* negative size, or sizes that do not fit together          */
-    LK_E_UNSUPPORTED = -3, /* valid request outside what this build implements:
+    LK_E_UNSUPPORTED = -3, /* valid request outside what the library implements:
                               heads != 64 in lk_index_score, T > LK_TOPK_MAX_T in
                               lk_topk, or a pointer not aligned to 16 bytes (4 for
                               float tensors)                                           */

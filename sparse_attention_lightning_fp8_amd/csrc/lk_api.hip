@@ -253,7 +253,7 @@ LK_API const char *lk_status_string(lk_status s) {
     case LK_OK: return "LK_OK";
     case LK_E_NULL: return "LK_E_NULL: a required pointer is NULL";
     case LK_E_SHAPE: return "LK_E_SHAPE: sizes are negative or do not fit together";
-    case LK_E_UNSUPPORTED: return "LK_E_UNSUPPORTED: outside what this build implements (heads, row length, alignment or grid limits)";
+    case LK_E_UNSUPPORTED: return "LK_E_UNSUPPORTED: outside what this library implements (heads, row length, alignment or grid limits)";
     case LK_E_HIP: return "LK_E_HIP: the HIP runtime rejected a kernel launch";
     }
     return "unknown lk_status";
