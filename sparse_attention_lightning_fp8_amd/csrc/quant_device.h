@@ -10,7 +10,7 @@
 // have 8-bit significands, so every partial sum is exact whenever the row's
 // magnitudes span at most 2^38, and the result does not depend on butterfly order.
 // Bits 0-3 of the feature index are combined in registers, bits 4-6 across the 8
-// lanes with xor-shuffles.  Every function here starts with fp contract(off): the
+// lanes with xor-shuffles (ds_bpermute or DPP, see cross_stage).  Every function here starts with fp contract(off): the
 // rounding steps must happen exactly where they are written, whatever the including
 // file's contraction setting.
 #pragma once
@@ -85,8 +85,59 @@ __device__ __forceinline__ int scale_exponent(double amax) {
     return j;
 }
 
+// Value of lane (lane ^ kM), kM = 1 .. 32: DPP quad_perm for 1 and 2, row_shl:4 /
+// row_shr:4 for 4, row_ror:8 for 8 (within a 16-lane row, lane i + 8 mod 16 is i ^ 8),
+// v_permlane16_swap for 16 (it returns rows (0, 0, 2, 2) and (1, 1, 3, 3)), and
+// v_permlane32_swap for 32 (the low half twice, the high half twice).
+template <int kM>
+__device__ __forceinline__ uint32_t wave_xor_u32(uint32_t x) {
+    const int lane = __lane_id();
+    if constexpr (kM == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (kM == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (kM == 4) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x104, 0xF, 0xF, false);
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
+        return (lane & 4) ? dn : up;
+    } else if constexpr (kM == 8) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
+    } else if constexpr (kM == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? p[0] : p[1];
+    } else {
+        static_assert(kM == 32, "xor distance 1 .. 32");
+        const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? p[0] : p[1];
+    }
+}
+template <int kM>
+__device__ __forceinline__ double wave_xor_f64(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint64_t lo = wave_xor_u32<kM>((uint32_t)u), hi = wave_xor_u32<kM>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+// One cross-lane butterfly stage of quantize_row16 (lane xor kM, kM = 1, 2 or 4) and
+// the matching step of the row's max.  The first kDppStages stages read the partner
+// through DPP quad_perm (VALU), the others through ds_bpermute (LDS): the preparation
+// kernel is bound by its LDS issue and moves two stages to DPP; the fused decode
+// kernel, whose VALU is the tighter pipe there, keeps all three on LDS.
+template <int kM, int kDppStages>
+__device__ __forceinline__ double lane_xor_f64(double x) {
+    if constexpr (kM < (1 << kDppStages)) return wave_xor_f64<kM>(x);
+    else return __shfl_xor(x, kM, 64);
+}
+template <int kM, int kDppStages>
+__device__ __forceinline__ void cross_stage(double (&x)[16]) {
+    const double sign = (__lane_id() & kM) ? -1.0 : 1.0;
+#pragma unroll
+    for (int e = 0; e < 16; e++) x[e] = butterfly_out(x[e], sign, lane_xor_f64<kM, kDppStages>(x[e]));   // upper: y - x; lower: x + y
+}
+
 // Quantize the row owned by this 8-lane group.  `in` holds the lane's 16 bf16 bit
 // patterns (8 dwords).  Returns the 16 codes packed in 4 dwords and the exponent j.
+// kDppStages: see cross_stage (the results do not depend on it).
+template <int kDppStages = 0>
 __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t out[4], int &j_out) {
 #pragma clang fp contract(off)
     double x[16];
@@ -107,16 +158,9 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
         }
     }
     // Cross-lane butterflies: feature-index bits 4..6 = lane bits 0..2.
-    const int lane = __lane_id();
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {
-        const double sign = (lane & m) ? -1.0 : 1.0;
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-            const double y = __shfl_xor(x[e], m, 64);
-            x[e] = butterfly_out(x[e], sign, y);           // upper: y - x; lower: x + y
-        }
-    }
+    cross_stage<1, kDppStages>(x);
+    cross_stage<2, kDppStages>(x);
+    cross_stage<4, kDppStages>(x);
     // Scale and round to bf16 (scale_round), and the row's amax.  p = r * C64 keeps the
     // sign of an exact zero sum; a -0 sum needs every input to be a zero (an exact
     // cancellation of nonzero terms rounds to +0), so only an all-zero row can hold
@@ -134,8 +178,9 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
         x[e] = x[e] * kRotScale;
         amax = __builtin_fmax(amax, __builtin_fabs(x[e]));
     }
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) amax = __builtin_fmax(amax, __shfl_xor(amax, m, 64));
+    amax = __builtin_fmax(amax, lane_xor_f64<1, kDppStages>(amax));
+    amax = __builtin_fmax(amax, lane_xor_f64<2, kDppStages>(amax));
+    amax = __builtin_fmax(amax, lane_xor_f64<4, kDppStages>(amax));
     const bool zero_row = amax == 0.0;                 // every input a zero (not: every p rounds to zero)
     if (__any(amax < 0x1p-108)) {
 #pragma unroll
@@ -248,38 +293,6 @@ __device__ __forceinline__ void rope_row16(uint32_t in[8], const Rope16 &r, int 
 // costs one wave a few hundred cycles instead of a full 16-feature pass.  Every lane
 // of the wave must take part (full EXEC).
 
-// Value of lane (lane ^ kM), kM = 1 .. 32: DPP quad_perm for 1 and 2, row_shl:4 /
-// row_shr:4 for 4, row_ror:8 for 8 (within a 16-lane row, lane i + 8 mod 16 is i ^ 8),
-// v_permlane16_swap for 16 (it returns rows (0, 0, 2, 2) and (1, 1, 3, 3)), and
-// v_permlane32_swap for 32 (the low half twice, the high half twice).
-template <int kM>
-__device__ __forceinline__ uint32_t wave_xor_u32(uint32_t x) {
-    const int lane = __lane_id();
-    if constexpr (kM == 1) {
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
-    } else if constexpr (kM == 2) {
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
-    } else if constexpr (kM == 4) {
-        const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x104, 0xF, 0xF, false);
-        const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
-        return (lane & 4) ? dn : up;
-    } else if constexpr (kM == 8) {
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
-    } else if constexpr (kM == 16) {
-        const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-        return (lane & 16) ? p[0] : p[1];
-    } else {
-        static_assert(kM == 32, "xor distance 1 .. 32");
-        const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-        return (lane & 32) ? p[0] : p[1];
-    }
-}
-template <int kM>
-__device__ __forceinline__ double wave_xor_f64(double x) {
-    const uint64_t u = (uint64_t)__double_as_longlong(x);
-    const uint64_t lo = wave_xor_u32<kM>((uint32_t)u), hi = wave_xor_u32<kM>((uint32_t)(u >> 32));
-    return __longlong_as_double((long long)((hi << 32) | lo));
-}
 template <int kM>
 __device__ __forceinline__ void wave_butterfly(double &x0, double &x1) {
 #pragma clang fp contract(off)

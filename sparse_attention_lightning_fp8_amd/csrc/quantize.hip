@@ -53,7 +53,7 @@ __device__ __forceinline__ void key_row(const KeyJob &k, int64_t g, int sub) {
     }
     uint32_t out[4];
     int j;
-    quantize_row16(in, out, j);
+    quantize_row16<2>(in, out, j);
     if (p < 0 || p >= k.cache_rows) return;
     const int64_t row = b * k.cache_seq_stride + p;
     *reinterpret_cast<uint4 *>(k.cache + row * LK_DIM + sub * 16) = make_uint4(out[0], out[1], out[2], out[3]);
@@ -73,7 +73,7 @@ __device__ __forceinline__ void query_row(const QueryJob &q, int64_t g, int sub)
     }
     uint32_t out[4];
     int j;
-    quantize_row16(in, out, j);
+    quantize_row16<2>(in, out, j);
     *reinterpret_cast<uint4 *>(q.q_fp8 + g * LK_DIM + sub * 16) = make_uint4(out[0], out[1], out[2], out[3]);
     if (sub == 0) {
         q.w_eff[g] = fold_weight(wg, j);
