@@ -5,12 +5,14 @@
 // [0, L) is selected exactly: the min(k, L) largest scores, ties to the lower index,
 // -0 equal to +0, unused slots -1.
 //
-// One block of 1024 threads per row.  The row is read from HBM once and stays in
-// registers: thread t holds elements 4(t + 1024 j) + c (j, c < 4).
+// One block per row, NT = 1024 threads, or 256 when T <= 4096 (short rows then keep
+// 16 scores per thread instead of leaving most of a large block idle).  The row is
+// read from HBM once and stays in registers: thread t holds elements 4(t + NT j) + c
+// (j, c < 4).
 //
 // 1. A block reduction finds the row's smallest and largest valid score, lo and hi.
-// 2. Each element goes to one of 4096 equal-width bins of [lo, hi]:
-//    bin(v) + 1 = trunc(fma(v - lo, 4095 * rcp(hi - lo), 1)), 1 .. 4096.  A rounded
+// 2. Each element goes to one of B = 4 NT equal-width bins of [lo, hi] (4096 or 1024):
+//    bin(v) + 1 = trunc(fma(v - lo, (B - 1) * rcp(hi - lo), 1)), 1 .. B.  A rounded
 //    subtraction, a correctly rounded fma with a positive factor and truncation are
 //    each monotone, so v1 < v2 implies bin(v1) <= bin(v2): every element of a higher
 //    bin outranks every element of a lower one.  Unlike digits of the float's bits,
@@ -19,9 +21,10 @@
 // 3. A block scan of the histogram from the top finds that bin b and how many of
 //    its elements are still needed.
 // 4. Inside bin b the exact cut is found: if the bin is taken whole, nothing more;
-//    if it holds at most 64 elements, they are ranked pairwise, 16 lanes per
-//    element (score descending, index ascending); otherwise a radix select walks the 32-bit
-//    order-preserving key of the bin's elements with digits of 12, 11 and 9 bits.
+//    if it holds at most 64 elements, they are ranked pairwise, NT / 64 lanes per
+//    element (score descending, index ascending); otherwise a radix select walks the
+//    32-bit order-preserving key of the bin's elements with digits of 12, 11 and 9 bits
+//    (10, 10, 10 and 2 with 1024 bins).
 //    A row whose range is empty or outside [1e-30, 1e30] puts every element in
 //    bin 0 and takes the radix path.
 // 5. The write-out ranks the selected elements with one block-wide scan of packed
@@ -39,11 +42,17 @@
 namespace lk {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kPer = 16;                    // elements per thread (kThreads * kPer == LK_TOPK_MAX_T)
-constexpr int kBins = 4096;
-constexpr int kSmall = 64;                  // a cut bin this small is ranked pairwise by one wave
+// Block shapes: NT threads (1024, or 256 for rows of at most 4096 scores), 16 scores
+// per thread, 4 histogram bins per thread.
+constexpr int kPer = 16;                    // elements per thread
+constexpr int kSmall = 64;                  // a cut bin this small is ranked pairwise
+template <int NT>
+struct Shape {
+    static constexpr int kThreads = NT, kWaves = NT / 64, kBins = 4 * NT, kMaxT = NT * kPer;
+    static constexpr int kLanesPerCand = NT / kSmall, kCandsPerLane = kSmall / kLanesPerCand;
+    static_assert(kWaves >= 4 && kWaves <= 16 && (kWaves & (kWaves - 1)) == 0, "one DPP row holds the wave totals");
+    static_assert(kCandsPerLane % 4 == 0, "16-byte candidate reads");
+};
 
 // Larger float -> larger key; -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float v) {
@@ -110,6 +119,7 @@ __device__ __forceinline__ float wave_fmin(float x) {
 
 // Sum of the per-wave totals of waves 0 .. wave-1 (before) and of all kWaves waves
 // (total), computed by every wave from the kWaves words of `part` (one per wave).
+template <int kWaves>
 __device__ __forceinline__ void wave_prefix(const uint32_t *part, int wave, uint32_t &before, uint32_t &total) {
     const int lane = __lane_id();
     const uint32_t s = row_scan16(lane < kWaves ? part[lane] : 0u);   // DPP row 0 holds them all
@@ -120,19 +130,20 @@ __device__ __forceinline__ void wave_prefix(const uint32_t *part, int wave, uint
 
 // Block-wide selection: the bin holding the need-th largest counted element (counting
 // from the top bin) and the number of counted elements in higher bins; writes
-// (bin, above, count) to sel.  Thread t owns bins 4095-4t .. 4092-4t (one 16-byte
-// read), scans within its wave with DPP and across waves through wsum.  Ends with a
-// barrier after which sel is valid.
+// (bin, above, count) to sel.  Thread t owns bins kBins-1-4t .. kBins-4-4t (one
+// 16-byte read), scans within its wave with DPP and across waves through wsum.  Ends
+// with a barrier after which sel is valid.
+template <int NT>
 __device__ __forceinline__ void select_bin(const uint32_t *hist, uint32_t need, uint32_t *wsum, uint32_t *sel) {
     const int tid = threadIdx.x, lane = __lane_id(), wave = tid >> 6;
-    const int lo = kBins - 4 - 4 * tid;                // bins lo .. lo+3, owned top-down
+    const int lo = Shape<NT>::kBins - 4 - 4 * tid;     // bins lo .. lo+3, owned top-down
     const uint4 h = *reinterpret_cast<const uint4 *>(hist + lo);
     const uint32_t mine = h.x + h.y + h.z + h.w;
     const uint32_t incl = wave_scan(mine);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     uint32_t before, total;
-    wave_prefix(wsum, wave, before, total);
+    wave_prefix<Shape<NT>::kWaves>(wsum, wave, before, total);
     uint32_t above = before + incl - mine;
     const uint32_t c[4] = {h.w, h.z, h.y, h.x};        // c[q] = bin lo+3-q
 #pragma unroll
@@ -148,17 +159,20 @@ __device__ __forceinline__ void select_bin(const uint32_t *hist, uint32_t need, 
 }
 
 __device__ __forceinline__ void clear_hist(uint32_t *hist) {
-    reinterpret_cast<uint4 *>(hist)[threadIdx.x] = make_uint4(0, 0, 0, 0);   // kThreads * 4 == kBins
+    reinterpret_cast<uint4 *>(hist)[threadIdx.x] = make_uint4(0, 0, 0, 0);   // 4 bins per thread
 }
 
 // Index of element e of thread tid.
+template <int NT>
 __device__ __forceinline__ uint32_t elem_index(int tid, int e) {
-    return 4u * tid + 4u * kThreads * (e >> 2) + (e & 3);
+    return 4u * tid + 4u * NT * (e >> 2) + (e & 3);
 }
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+template <int NT>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8)))
 topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *__restrict__ idx) {
-    static_assert(kThreads * 4 == kBins && kThreads * kPer == LK_TOPK_MAX_T && kWaves == 16, "tiling");
+    constexpr int kThreads = Shape<NT>::kThreads, kWaves = Shape<NT>::kWaves, kBins = Shape<NT>::kBins;
+    constexpr int kLanesPerCand = Shape<NT>::kLanesPerCand, kCandsPerLane = Shape<NT>::kCandsPerLane;
     __shared__ __attribute__((aligned(16))) uint32_t hist_buf[4 + kBins];   // word 3: invalid elements
     uint32_t *const hist = hist_buf + 4;                                     // bins 0 .. kBins-1
     __shared__ __attribute__((aligned(16))) uint32_t wtot[kWaves][4];
@@ -180,7 +194,7 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
         for (int64_t j = tid; j < k; j += kThreads) out[j] = j < L ? (int32_t)j : -1;
         return;
     }
-    const int n = (int)L;                              // k < L <= T <= LK_TOPK_MAX_T
+    const int n = (int)L;                              // k < L <= T <= Shape<NT>::kMaxT (host choice)
     const float *src = scores + (int64_t)row * T;
 
     clear_hist(hist);
@@ -239,18 +253,17 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
         wred[1][wave] = mn;
     }
     __syncthreads();
-    // Every wave reduces the kWaves partial results itself (lane l reads wave l % 16,
-    // so one DPP row holds all of them).
-    static_assert(kWaves == 16, "one DPP row per block reduction");
+    // Every wave reduces the kWaves partial results itself (lane l reads wave
+    // l % kWaves, so one DPP row holds all of them).
     mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row_fmax16(wred[0][lane & (kWaves - 1)])), 15));
     mn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row_fmin16(wred[1][lane & (kWaves - 1)])), 15));
     const float width = mx - mn;
     const bool spread = width >= 1e-30f && width <= 1e30f;
-    // scale = 4095 * rcp(width), the hardware reciprocal (within 1 ulp), keeps
-    // fma(v - mn, scale, 1) below 4097, and every valid score of a spread row is finite,
-    // so bin + 1 is 1 .. 4096; it is monotone in v (a rounded subtraction, then a
-    // correctly rounded fma with a positive factor, then truncation).
-    const float scale = 4095.f * __builtin_amdgcn_rcpf(width);
+    // scale = (kBins - 1) * rcp(width), the hardware reciprocal (within 1 ulp), keeps
+    // fma(v - mn, scale, 1) below kBins + 1, and every valid score of a spread row is
+    // finite, so bin + 1 is 1 .. kBins; it is monotone in v (a rounded subtraction,
+    // then a correctly rounded fma with a positive factor, then truncation).
+    const float scale = (float)(kBins - 1) * __builtin_amdgcn_rcpf(width);
 
     // 2-3. Histogram of the bins (invalid elements count in hist[-1], a spare word),
     //      then the bin holding the k-th largest.
@@ -277,7 +290,7 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
         }
     }
     __syncthreads();
-    select_bin(hist, (uint32_t)k, wsum, sel);
+    select_bin<NT>(hist, (uint32_t)k, wsum, sel);
     const uint32_t cb = sel[0], cnt = sel[2];
     uint32_t need = (uint32_t)k - sel[1];
 
@@ -299,31 +312,41 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
             const int e = __builtin_ctz(m);
             const uint32_t slot = atomicAdd(&ccount, 1u);
             cand_key[slot] = order_key(v[e]);
-            cand_idx[slot] = elem_index(tid, e);
+            cand_idx[slot] = elem_index<NT>(tid, e);
         }
         __syncthreads();
-        // Rank of candidate ci = tid / 16 among all candidates (score descending, index
-        // ascending): the 16 lanes of a DPP row each compare it with 4 candidates and
-        // the row sums the packed counts (above: low half, equal with a lower index: high).
+        // Rank of candidate ci = tid / kLanesPerCand among all candidates (score
+        // descending, index ascending): its kLanesPerCand consecutive lanes each compare
+        // it with kCandsPerLane candidates and sum the packed counts (above: low half,
+        // equal with a lower index: high half).
         {
-            const int ci = tid >> 4, q = tid & 15;
+            const int ci = tid / kLanesPerCand, q = tid % kLanesPerCand;
             uint32_t packed = 0, mk = 0, mi = 0;
             if (ci < (int)cnt) {
                 mk = cand_key[ci];
                 mi = cand_idx[ci];
-                const uint4 kq = *reinterpret_cast<const uint4 *>(cand_key + 4 * q);
-                const uint4 iq = *reinterpret_cast<const uint4 *>(cand_idx + 4 * q);
-                const uint32_t kj[4] = {kq.x, kq.y, kq.z, kq.w}, ij[4] = {iq.x, iq.y, iq.z, iq.w};
 #pragma unroll
-                for (int jj = 0; jj < 4; jj++) {
-                    if (4 * q + jj < (int)cnt) {
-                        packed += kj[jj] > mk ? 1u : 0u;
-                        packed += (kj[jj] == mk && ij[jj] < mi) ? 0x10000u : 0u;
+                for (int c4 = 0; c4 < kCandsPerLane / 4; c4++) {
+                    const int c0 = kCandsPerLane * q + 4 * c4;
+                    const uint4 kq = *reinterpret_cast<const uint4 *>(cand_key + c0);
+                    const uint4 iq = *reinterpret_cast<const uint4 *>(cand_idx + c0);
+                    const uint32_t kj[4] = {kq.x, kq.y, kq.z, kq.w}, ij[4] = {iq.x, iq.y, iq.z, iq.w};
+#pragma unroll
+                    for (int jj = 0; jj < 4; jj++) {
+                        if (c0 + jj < (int)cnt) {
+                            packed += kj[jj] > mk ? 1u : 0u;
+                            packed += (kj[jj] == mk && ij[jj] < mi) ? 0x10000u : 0u;
+                        }
                     }
                 }
             }
-            packed = row_scan16(packed);
-            if (q == 15 && ci < (int)cnt) {
+            if constexpr (kLanesPerCand == 16) {
+                packed = row_scan16(packed);               // lane 15 of the DPP row ends with the sum
+            } else {
+#pragma unroll
+                for (int d = 1; d < kLanesPerCand; d <<= 1) packed += (uint32_t)__shfl_xor((int)packed, d, 64);
+            }
+            if (q == kLanesPerCand - 1 && ci < (int)cnt) {
                 const uint32_t gt = packed & 0xFFFFu, eq_before = packed >> 16;
                 if (gt + eq_before == need - 1) {      // the need-th candidate: the cut
                     cut[0] = mk;
@@ -336,18 +359,22 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
         pmask = 0xFFFFFFFFu;
         need = cut[1];
     } else if (need < cnt) {
+        // Digits of at most log2(kBins) bits from the top: key bits 31-20, 19-9, 8-0 with
+        // 4096 bins; 31-22, 21-12, 11-2, 1-0 with 1024.
+        constexpr int kPasses = kBins == 4096 ? 3 : 4;
+        static_assert(kBins == 4096 || kBins == 1024, "digit plan");
 #pragma unroll 1
-        for (int pass = 0; pass < 3; pass++) {       // digits: key bits 31-20, 19-9, 8-0
+        for (int pass = 0; pass < kPasses; pass++) {
             clear_hist(hist);
             __syncthreads();
-            const int sh = pass == 0 ? 20 : pass == 1 ? 9 : 0;
-            const uint32_t dm = pass == 0 ? 0xFFFu : pass == 1 ? 0x7FFu : 0x1FFu;
+            const int sh = kBins == 4096 ? (pass == 0 ? 20 : pass == 1 ? 9 : 0) : (pass == 3 ? 0 : 22 - 10 * pass);
+            const uint32_t dm = kBins == 4096 ? (pass == 0 ? 0xFFFu : pass == 1 ? 0x7FFu : 0x1FFu) : (pass == 3 ? 0x3u : 0x3FFu);
             for (uint32_t m = ebits; m; m &= m - 1) {
                 const uint32_t kk = order_key(v[__builtin_ctz(m)]);
                 if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> sh) & dm], 1u);
             }
             __syncthreads();
-            select_bin(hist, need, wsum, sel);
+            select_bin<NT>(hist, need, wsum, sel);
             const uint32_t d = sel[0], ab = sel[1], dcnt = sel[2];
             need -= ab;
             prefix |= d << sh;
@@ -431,7 +458,9 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
 
 hipError_t launch_topk(const float *scores, const RowsDev &rows, int32_t k, int32_t *idx, hipStream_t stream) {
     const unsigned nrows = (unsigned)((int64_t)rows.B * rows.S);
-    return launch(topk_kernel, dim3(nrows), dim3(kThreads), 0u, stream, scores, rows, k, idx);
+    if (rows.T <= Shape<256>::kMaxT)
+        return launch(topk_kernel<256>, dim3(nrows), dim3(256), 0u, stream, scores, rows, k, idx);
+    return launch(topk_kernel<1024>, dim3(nrows), dim3(1024), 0u, stream, scores, rows, k, idx);
 }
 
 }  // namespace lk

@@ -39,9 +39,9 @@ def test_topk_random_rows_exact(T, k):
     _check_exact(scores, k, _gpu_topk(scores, k), None)
 
 
-def test_topk_ties_signed_zeros_and_infinities():
+@pytest.mark.parametrize("T", [5000, 3000])          # the 1024- and the 256-thread kernel
+def test_topk_ties_signed_zeros_and_infinities(T):
     rng = np.random.default_rng(5)
-    T = 5000
     s = rng.integers(-4, 4, (3, 2, T)).astype(np.float32)      # heavy ties
     s[0, 0, ::2] = -0.0
     s[0, 0, 1::2] = 0.0
@@ -49,8 +49,8 @@ def test_topk_ties_signed_zeros_and_infinities():
     s[1, 1, 17] = 1.0
     s[2, 0, :] = 3.0                                           # all equal
     s[2, 1, 100:] = -np.inf
-    log("[topk] ties")
-    for k in (1, 7, 2048, 4999):
+    log(f"[topk] ties T={T}")
+    for k in (1, 7, 2048, T - 1):
         _check_exact(s, k, _gpu_topk(s, k), None)
 
 
@@ -90,15 +90,16 @@ def test_topk_deterministic_and_ordered():
             assert ok, (bi, ti)
 
 
-def test_topk_cut_paths():
+@pytest.mark.parametrize("T", [8192, 4096])          # the 1024- and the 256-thread kernel
+def test_topk_cut_paths(T):
     """Rows built so that the bin holding the k-th largest score is taken whole, holds a
     few elements (ranked pairwise) or many (radix passes), or the row has no spread."""
     rng = np.random.default_rng(8)
-    T, k = 8192, 1000
+    k = 1000
     rows = []
     base = rng.standard_normal(T).astype(np.float32)
     rows.append(base)                                          # a few elements in the cut bin
-    r = np.arange(T, dtype=np.float32)                         # one value per bin: cut bin taken whole
+    r = np.arange(T, dtype=np.float32)                         # evenly spaced: every bin holds the same few
     rows.append(rng.permutation(r))
     crowd = base.copy()
     crowd[rng.choice(T, 3000, replace=False)] = 0.5            # ~3000 equal values straddle the cut
@@ -114,6 +115,6 @@ def test_topk_cut_paths():
     tiny = (base * 1e-33).astype(np.float32)                   # range below 1e-30
     rows.append(tiny)
     s = np.stack(rows)[:, None, :]
-    log("[topk] cut paths")
+    log(f"[topk] cut paths T={T}")
     for kk in (k, 1, 64, 65, 4096):
         _check_exact(s, kk, _gpu_topk(s, kk), None)
