@@ -20,8 +20,9 @@
  *     or synchronizes; each call only enqueues kernels on `stream` and returns.
  *   - `lk_rows` structures are HOST memory, read during the call only.
  *   - Validation happens on the host before any HIP call; a failed validation
- *     enqueues nothing.  LK_E_HIP reports a failed kernel launch
- *     (hipGetLastError() after the launch).
+ *     enqueues nothing.  LK_E_HIP reports a failed kernel launch (the status the
+ *     launch call itself returned; errors pending from earlier HIP calls are not
+ *     read or cleared).
  *   - bf16 data is passed as its uint16 bit pattern; fp8 data is e4m3fn bytes.
  *   - The library keeps no state (apart from the per-thread profiling events of
  *     lk_profile_next_launch), prints nothing and never aborts; calls are
@@ -55,8 +56,8 @@ typedef enum lk_status {
     LK_E_SHAPE = -2,       /* negative size, or sizes that do not fit together          */
     LK_E_UNSUPPORTED = -3, /* valid request outside what the library implements:
                               heads != 64 in lk_index_score, T > LK_TOPK_MAX_T in
-                              lk_topk, or a pointer not aligned to 16 bytes (4 for
-                              float tensors)                                           */
+                              lk_topk, a launch grid beyond the HIP limits, or a
+                              pointer not aligned to 16 bytes (4 for float tensors)    */
     LK_E_HIP = -4          /* the HIP runtime rejected a kernel launch                 */
 } lk_status;
 
@@ -93,8 +94,12 @@ typedef struct lk_rows {
  * (nearest-even, sign kept, never NaN).  The 128 bytes go to cache row
  *   p = (positions ? positions[b] : row_offset) + i
  * at  cache + (b * cache_seq_stride + p) * 128, and 2^j to
- * cache_scale[b * cache_seq_stride + p].  Rows with p outside [0, cache_rows)
- * are skipped (not written).  positions is DEVICE [n_seq] int32 or NULL.
+ * cache_scale[b * cache_seq_stride + p].  positions is DEVICE [n_seq] int32 or NULL.
+ * Without positions the host checks the destination: 0 <= row_offset and
+ * row_offset + n_rows <= cache_rows, else LK_E_SHAPE (the cache write at
+ * [start_pos, end_pos) of Indexer.forward never leaves the cache).  With positions,
+ * which the host cannot read, the kernel checks each row and skips (does not write)
+ * a row whose p falls outside [0, cache_rows).
  * Results are bit-exact for every row whose nonzero magnitudes span at most
  * 2^38 and whose values are below 2^120 in magnitude.
  * Requires: cache_rows <= cache_seq_stride; x and cache 16-byte aligned.
@@ -158,7 +163,8 @@ LK_API lk_status lk_prepare(const uint16_t *x, int64_t n_seq, int64_t n_rows, in
  * with float32 accumulation; ReLU, the head weighting and sum, the key scale and
  * the mask are applied in registers; each score is written once.
  * Requires heads == 64 (else LK_E_UNSUPPORTED), T <= cache_seq_stride,
- * q_fp8 and k_cache 16-byte aligned, w_eff 16-byte aligned.
+ * q_fp8 and k_cache 16-byte aligned, w_eff 16-byte aligned.  LK_E_UNSUPPORTED past
+ * the launch grid limits: B > 65535, or (S > 1) ceil(S / 4) > 65535.
  */
 LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_t heads,
                                 const uint8_t *k_cache, const float *k_scale,
@@ -202,7 +208,9 @@ LK_API lk_status lk_decode_score(const uint16_t *q, const float *w, int32_t head
  * each in increasing index order: an upper group, then a cut group; every score
  * of the upper group is above every score of the cut group, and within the cut
  * group's lowest score the lower indices are the ones taken.
- * Requires k >= 1 and T <= LK_TOPK_MAX_T (else LK_E_UNSUPPORTED).
+ * Requires 1 <= k <= T (else LK_E_SHAPE: the reference asks for
+ * min(index_topk, end_pos) entries, never more than the row holds) and
+ * T <= LK_TOPK_MAX_T (else LK_E_UNSUPPORTED).
  */
 LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, int32_t *idx,
                          hipStream_t stream);

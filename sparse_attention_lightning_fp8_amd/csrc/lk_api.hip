@@ -9,6 +9,7 @@ hipError_t launch_quantize(const KeyJobArgs &ka, const QueryJobArgs &qa, hipStre
 hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
                               const float *k_scale, int64_t cache_seq_stride, const RowsDev &rows,
                               float *scores, hipStream_t stream);
+bool index_score_grid_fits(const RowsDev &rows);
 hipError_t launch_topk(const float *scores, const RowsDev &rows, int32_t k, int32_t *idx, hipStream_t stream);
 hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t *k_new, uint8_t *k_cache,
                                float *k_scale, int64_t cache_seq_stride, const RowsDev &rows, float *scores,
@@ -79,6 +80,9 @@ lk_status check_keys(const uint16_t *x, int64_t n_seq, int64_t n_rows, int64_t x
     if (!aligned(x, 16) || !aligned(cache, 16) || !aligned(cache_scale, 4) || !aligned(positions, 4))
         return LK_E_UNSUPPORTED;
     if (n_rows > INT64_MAX / n_seq || (n_seq * n_rows + 31) / 32 > kMaxGridX / 2) return LK_E_UNSUPPORTED;
+    // A host-known destination must fit the cache; device positions are checked per row
+    // by the kernel, which skips rows outside [0, cache_rows).
+    if (!positions && (row_offset < 0 || row_offset > cache_rows - n_rows)) return LK_E_SHAPE;
     a = lk::KeyJobArgs{x, n_seq, n_rows, x_seq_stride, cache, cache_scale, cache_seq_stride, cache_rows,
                        row_offset, positions};
     return LK_OK;
@@ -174,8 +178,7 @@ LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_
     if (!aligned(q_fp8, 16) || !aligned(w_eff, 16) || !aligned(k_cache, 16) || !aligned(k_scale, 4) ||
         !aligned(scores, 4) || !aligned(rows->seq_len, 4))
         return LK_E_UNSUPPORTED;
-    if (rows->B > kMaxGridYZ || (rows->S + 7) / 8 > kMaxGridYZ) return LK_E_UNSUPPORTED;
-    if (rows->T > kMaxGridX) return LK_E_UNSUPPORTED;
+    if (rows->T > kMaxGridX || !lk::index_score_grid_fits(to_dev(*rows))) return LK_E_UNSUPPORTED;
     return from_hip(lk::launch_index_score(q_fp8, w_eff, k_cache, k_scale, cache_seq_stride, to_dev(*rows),
                                            scores, stream));
 }
@@ -209,7 +212,7 @@ LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, in
     DisarmOnExit disarm;
     lk_status st = check_rows(rows);
     if (st != LK_OK) return st;
-    if (k < 1) return LK_E_SHAPE;
+    if (k < 1 || k > rows->T) return LK_E_SHAPE;
     if (rows->T > LK_TOPK_MAX_T) return LK_E_UNSUPPORTED;
     if (rows->B == 0 || rows->S == 0) return LK_OK;
     if (!scores || !idx) return LK_E_NULL;

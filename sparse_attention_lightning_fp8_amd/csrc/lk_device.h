@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 #include "lk.h"
 
 namespace lk {
@@ -109,17 +111,27 @@ struct LaunchEvents {
 LaunchEvents &armed_events();
 
 // Launch on `stream`; if events are armed, they are recorded at the kernel's own start
-// and end (hipExtLaunchKernel) and disarmed.  Returns the launch status.
-template <typename F, typename... Args>
-hipError_t launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t stream, Args... args) {
+// and end (hipExtLaunchKernel) and disarmed.  Returns the status of this launch call
+// itself (not an error left pending by earlier, unrelated HIP calls).  The arguments
+// are converted to the kernel's parameter types before their addresses are taken.
+template <typename... Params, typename... Args>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t shm, hipStream_t stream,
+                  Args... args) {
+    static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+    std::tuple<Params...> vals{static_cast<Params>(args)...};
+    void *argv[sizeof...(Params) > 0 ? sizeof...(Params) : 1] = {};
+    std::apply([&argv](auto &...v) {
+        int i = 0;
+        ((argv[i++] = static_cast<void *>(&v)), ...);
+    }, vals);
     LaunchEvents &ev = armed_events();
     if (ev.start && ev.stop) {
-        hipExtLaunchKernelGGL(kernel, grid, block, shm, stream, ev.start, ev.stop, 0u, args...);
+        const LaunchEvents use = ev;
         ev = LaunchEvents{};
-    } else {
-        hipLaunchKernelGGL(kernel, grid, block, shm, stream, args...);
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, shm, stream,
+                                  use.start, use.stop, 0);
     }
-    return hipGetLastError();
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, shm, stream);
 }
 
 }  // namespace lk

@@ -45,11 +45,18 @@ __device__ __forceinline__ lk_v2i16 encode_e4m3_pair(lk_v2i16 old, float a, floa
     return __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, a, b, 1.0f, kHi);
 }
 
-// A rotated feature (its exact Hadamard sum) times 128^-0.5, rounded once to bf16; an
-// exact zero sum is +0.
+// A rotated feature (its exact Hadamard sum) times 128^-0.5 in one rounding, with an
+// exact zero sum (of either sign) made +0: r * C + (+0) rounds the product once and
+// turns only a -0 into +0, since a nonzero product plus zero is itself.  The fma is not
+// folded into a plain multiply (that would keep -0).
+__device__ __forceinline__ double scale_rot(double r) {
+    return __builtin_fma(r, kRotScale, 0.0);
+}
+
+// scale_rot, then one rounding to bf16.
 __device__ __forceinline__ double scale_round(double r) {
 #pragma clang fp contract(off)
-    return round_to_bf16((r == 0.0 ? 0.0 : r) * kRotScale);
+    return round_to_bf16(scale_rot(r));
 }
 
 // Nearest even to 8 significant bits straight on the fp64 bits (add half an ulp at
@@ -161,11 +168,11 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
     cross_stage<1, kDppStages>(x);
     cross_stage<2, kDppStages>(x);
     cross_stage<4, kDppStages>(x);
-    // Scale and round to bf16 (scale_round), and the row's amax.  p = r * C64 keeps the
-    // sign of an exact zero sum; a -0 sum needs every input to be a zero (an exact
-    // cancellation of nonzero terms rounds to +0), so only an all-zero row can hold
-    // one, and its codes are set to +0 below.  (A nonzero p that rounds to zero keeps
-    // its sign.)
+    // Scale and round to bf16 (scale_round), and the row's amax.  An exact zero sum can
+    // come out of the butterflies as -0 in any row (a sum or difference of zeros drawn
+    // from -0 inputs, such as a zero RoPE pair with a negative cosine, next to nonzero
+    // features elsewhere), so scale_rot makes every exact zero +0 here, as the
+    // definition's sum is.  (A nonzero p that rounds to zero keeps its sign.)
     // The bit rounding is exact for every nonzero |p| >= 2^-126.  A nonzero p below
     // that only matters when the scale exponent is -117 or less (otherwise both
     // roundings, at most 2^-126 in magnitude, times 2^-j <= 2^-10, encode to a zero of
@@ -175,13 +182,12 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
     double amax = 0.0;
 #pragma unroll
     for (int e = 0; e < 16; e++) {
-        x[e] = x[e] * kRotScale;
+        x[e] = scale_rot(x[e]);
         amax = __builtin_fmax(amax, __builtin_fabs(x[e]));
     }
     amax = __builtin_fmax(amax, lane_xor_f64<1, kDppStages>(amax));
     amax = __builtin_fmax(amax, lane_xor_f64<2, kDppStages>(amax));
     amax = __builtin_fmax(amax, lane_xor_f64<4, kDppStages>(amax));
-    const bool zero_row = amax == 0.0;                 // every input a zero (not: every p rounds to zero)
     if (__any(amax < 0x1p-108)) {
 #pragma unroll
         for (int e = 0; e < 16; e++) x[e] = round_to_bf16(x[e]);
@@ -201,7 +207,7 @@ __device__ __forceinline__ void quantize_row16(const uint32_t in[8], uint32_t ou
         lk_v2i16 w = {0, 0};
         w = encode_e4m3_pair<false>(w, q[0], q[1]);
         w = encode_e4m3_pair<true>(w, q[2], q[3]);
-        out[i] = zero_row ? 0u : __builtin_bit_cast(uint32_t, w);   // an all-zero row: +0 codes
+        out[i] = __builtin_bit_cast(uint32_t, w);
     }
 }
 

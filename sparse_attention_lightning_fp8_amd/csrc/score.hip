@@ -610,6 +610,13 @@ hipError_t launch_decode_grid(const DecodeArgs &a, hipStream_t stream) {
 
 }  // namespace
 
+// Whether lk_index_score's grid for these rows is within the launch limits.
+bool index_score_grid_fits(const RowsDev &rows) {
+    if (rows.B > 65535) return false;
+    if (rows.S == 1) return (rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock <= 0x7FFFFFFF;
+    return (rows.S + kPreWaves - 1) / kPreWaves <= 65535 && (rows.T + kPreSlice - 1) / kPreSlice <= 0x7FFFFFFF;
+}
+
 hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
                               const float *k_scale, int64_t cache_seq_stride, const RowsDev &rows,
                               float *scores, hipStream_t stream) {

@@ -61,6 +61,14 @@ def test_quantize_keys_validation(lib):
     assert f(A, 1, 1, 1, A + 4, A, 16, 16, 0, None, None) == E_UNSUP
     assert f(A, 1, 1, 1, A, A, 16, 16, 0, A + 2, None) == E_UNSUP        # misaligned positions
     assert f(None, 0, 5, 0, None, None, 0, 0, 0, None, None) == OK        # empty: nothing to do
+    # a host-known destination must fit the cache: rows [row_offset, row_offset + n_rows)
+    assert f(A, 2, 5, 5, A, A, 16, 16, 12, None, None) == E_SHAPE         # 12 + 5 > 16
+    assert f(A, 1, 17, 17, A, A, 16, 16, 0, None, None) == E_SHAPE        # more rows than the cache
+    assert f(A, 1, 1, 1, A, A, 16, 16, -1, None, None) == E_SHAPE         # negative offset
+    assert f(A, 1, 1, 1, A, A, 16, 16, 1 << 62, None, None) == E_SHAPE    # no overflow in the check
+    # device positions are the kernel's to check (rows outside the cache are skipped):
+    # the same sizes pass validation and only then fail on the fake pointers' alignment
+    assert f(A, 2, 5, 5, A, A, 16, 16, 12, A + 2, None) == E_UNSUP
 
 
 def test_quantize_queries_validation(lib):
@@ -105,6 +113,9 @@ def test_index_score_validation(lib):
     assert f(A, A + 4, 64, A, A, 16, rows(), A, None) == E_UNSUP
     assert f(A, A, 64, A, A, 16, rows(seq_len=A + 1), A, None) == E_UNSUP
     assert f(A, A, 64, A, A, 70000, rows(B=70000, T=16), A, None) == E_UNSUP  # grid limit
+    # prefill grid: one block row per four query tokens, at most 65535
+    assert f(A, A, 64, A, A, 16, rows(S=4 * 65535 + 1, T=16), A + 8, None) == E_UNSUP   # alignment first
+    assert f(A, A, 64, A, A, 16, rows(S=4 * 65535, T=16, seq_len=A + 2), A, None) == E_UNSUP
     assert f(None, None, 64, None, None, 16, rows(B=0), None, None) == OK
     assert f(None, None, 64, None, None, 16, rows(T=0), None, None) == OK
 
@@ -134,6 +145,7 @@ def test_topk_validation(lib):
     f = lib.lk_topk
     assert f(A, None, 8, A, None) == E_NULL
     assert f(A, rows(), 0, A, None) == E_SHAPE
+    assert f(A, rows(T=16), 17, A, None) == E_SHAPE                          # k beyond the row (k <= T)
     assert f(A, rows(S=-2), 8, A, None) == E_SHAPE
     assert f(A, rows(T=16385), 8, A, None) == E_UNSUP
     assert f(None, rows(), 8, A, None) == E_NULL

@@ -206,6 +206,21 @@ def test_quantize_scale_equivariance():
         assert np.array_equal(cm, c0) and np.array_equal(sm, s0 * np.float32(2.0**m))
 
 
+def test_quantize_exact_zero_sums_are_plus_zero():
+    """Closed form of the row [-0, +0, 1, 1, 0, ...]: r_j = s(j & 2) + s(j & 3) with
+    s(m) = (-1)^popcount(m), so every odd j sums to exactly zero (code 0x00, never 0x80)
+    and every even j to +-2 (2 / sqrt(128) -> bf16 0.1767578125 = 362 * 2^-11, so
+    scale 2^-11 and code 0x7B (352) or 0xFB).  The same with -0 in every empty slot."""
+    exp = np.array([0 if j & 1 else (0xFB if j & 2 else 0x7B) for j in range(128)], np.uint8)
+    one = np.uint16(0x3F80)
+    for fill in (0x0000, 0x8000):
+        row = np.full(128, fill, np.uint16)
+        row[0], row[1], row[2], row[3] = 0x8000, 0x0000, one, one
+        codes, scales = O.quantize_rows(row[None, :])
+        assert np.array_equal(codes[0], exp)
+        assert scales[0] == np.float32(2.0 ** -11)
+
+
 def test_quantize_properties_random_rows():
     g = torch.Generator().manual_seed(6)
     x = torch.randn(256, 128, generator=g).to(torch.bfloat16)

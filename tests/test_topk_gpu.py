@@ -31,7 +31,7 @@ def _check_exact(scores, k, gidx, lens=None, causal=False, start_pos=0):
 
 
 @pytest.mark.parametrize("T,k", [(1, 1), (5, 2), (1001, 256), (2049, 2048), (4096, 2048), (16384, 2048),
-                                 (16384, 1), (16384, 16384), (3000, 4000)])
+                                 (16384, 1), (16384, 16384), (3000, 3000)])
 def test_topk_random_rows_exact(T, k):
     rng = np.random.default_rng(T + k)
     scores = rng.standard_normal((2, 3, T)).astype(np.float32)
