@@ -49,6 +49,7 @@ extern "C" {
 #define LK_MLA_HEADS 128    /* attention heads of the MLA decode (page "Join query parts") */
 #define LK_MLA_LATENT 512   /* latent (content) features per head and per cached row    */
 #define LK_MLA_ROPE 64      /* rotary features per head and per cached row              */
+#define LK_MLA_SCRATCH_BYTES (64u << 20) /* static workspace of lk_sparse_mla_decode_static */
 
 typedef enum lk_status {
     LK_OK = 0,
@@ -58,7 +59,9 @@ typedef enum lk_status {
                               heads != 64 in lk_index_score, T > LK_TOPK_MAX_T in
                               lk_topk, a launch grid beyond the HIP limits, or a
                               pointer not aligned to 16 bytes (4 for float tensors)    */
-    LK_E_HIP = -4          /* the HIP runtime rejected a kernel launch                 */
+    LK_E_HIP = -4,         /* the HIP runtime rejected a kernel launch                 */
+    LK_E_SCRATCH = -5      /* lk_sparse_mla_decode_static: the request needs more
+                              workspace than LK_MLA_SCRATCH_BYTES                      */
 } lk_status;
 
 /*
@@ -242,6 +245,27 @@ LK_API lk_status lk_sparse_mla_decode(const uint16_t *q_latent, const uint16_t *
                                       const uint16_t *kv_rope, int64_t cache_seq_stride, int64_t cache_rows,
                                       const int32_t *idx, int32_t B, int32_t n_idx, float scale, float *out,
                                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lk_sparse_mla_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the per-split partials go to a static buffer of
+ * LK_MLA_SCRATCH_BYTES (64 MiB) that the library holds on each device from the first
+ * use until the process ends.  Arguments and results are those of
+ * lk_sparse_mla_decode minus the workspace; the output is the same, bit for bit.
+ * LK_E_SCRATCH when lk_sparse_mla_workspace_size(B, n_idx) > LK_MLA_SCRATCH_BYTES
+ * (for example B = 16 with n_idx = 2048 needs 33.7 MB and fits; B = 32 does not).
+ * The call allocates nothing (no hipMalloc, no hipFree); the buffer's device address
+ * is looked up once per device (hipGetSymbolAddress), on the current device, which
+ * must be the one `stream` runs on.  Every call on a device shares that device's
+ * buffer: calls that overlap on one device (other streams, other threads) race and
+ * must be serialised by the caller.  The buffer needs no clearing between calls.
+ */
+LK_API lk_status lk_sparse_mla_decode_static(const uint16_t *q_latent, const uint16_t *q_rope,
+                                             const uint16_t *kv_latent, const uint16_t *kv_rope,
+                                             int64_t cache_seq_stride, int64_t cache_rows, const int32_t *idx,
+                                             int32_t B, int32_t n_idx, float scale, float *out,
+                                             hipStream_t stream);
 
 /*
  * Profiling aid, outside the indexer computation: arm two HIP events for the next

@@ -10,7 +10,8 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblk.so")
 
 LK_OK = 0
-STATUS_NAMES = {0: "LK_OK", -1: "LK_E_NULL", -2: "LK_E_SHAPE", -3: "LK_E_UNSUPPORTED", -4: "LK_E_HIP"}
+STATUS_NAMES = {0: "LK_OK", -1: "LK_E_NULL", -2: "LK_E_SHAPE", -3: "LK_E_UNSUPPORTED", -4: "LK_E_HIP",
+                -5: "LK_E_SCRATCH"}
 
 # Every function the header declares, as (name, restype, argtypes).
 _p = ctypes.c_void_p
@@ -36,6 +37,8 @@ SIGNATURES = {
     "lk_sparse_mla_workspace_size": (ctypes.c_size_t, [_i32, _i32]),
     "lk_sparse_mla_decode": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _i32, ctypes.c_float, _p, _p,
                                             ctypes.c_size_t, _p]),
+    "lk_sparse_mla_decode_static": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _i32, ctypes.c_float,
+                                                   _p, _p]),
     "lk_profile_next_launch": (ctypes.c_int, [_p, _p]),
     "lk_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lk_abi_version": (_i32, []),

@@ -16,6 +16,10 @@ hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t
                                uint8_t *q_fp8_out, float *w_eff_out, const float *rope_cos,
                                const float *rope_sin, hipStream_t stream);
 size_t mla_workspace_bytes(int32_t B, int32_t n_idx);
+size_t mla_scratch_capacity();
+hipError_t launch_sparse_mla_static(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *kv_lat,
+                                    const uint16_t *kv_rope, int64_t stride, int64_t cap, const int32_t *idx,
+                                    int32_t B, int32_t n_idx, float scale, float *out, hipStream_t stream);
 bool mla_grid_fits(int32_t B, int32_t n_idx);
 hipError_t launch_sparse_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *kv_lat,
                              const uint16_t *kv_rope, int64_t stride, int64_t cap, const int32_t *idx, int32_t B,
@@ -245,6 +249,25 @@ LK_API lk_status lk_sparse_mla_decode(const uint16_t *q_latent, const uint16_t *
                                           n_idx, scale, out, workspace, stream));
 }
 
+LK_API lk_status lk_sparse_mla_decode_static(const uint16_t *q_latent, const uint16_t *q_rope,
+                                             const uint16_t *kv_latent, const uint16_t *kv_rope,
+                                             int64_t cache_seq_stride, int64_t cache_rows, const int32_t *idx,
+                                             int32_t B, int32_t n_idx, float scale, float *out,
+                                             hipStream_t stream) {
+    DisarmOnExit disarm;
+    if (B < 0 || n_idx < 0 || cache_seq_stride < 0 || cache_rows < 0) return LK_E_SHAPE;
+    if (cache_rows > cache_seq_stride) return LK_E_SHAPE;
+    if (B == 0) return LK_OK;
+    if (!q_latent || !q_rope || !out || (n_idx > 0 && (!kv_latent || !kv_rope || !idx))) return LK_E_NULL;
+    if (!aligned(q_latent, 16) || !aligned(q_rope, 16) || !aligned(kv_latent, 16) || !aligned(kv_rope, 16) ||
+        !aligned(out, 16) || !aligned(idx, 4))
+        return LK_E_UNSUPPORTED;
+    if (B > kMaxGridYZ || !lk::mla_grid_fits(B, n_idx)) return LK_E_UNSUPPORTED;
+    if (lk_sparse_mla_workspace_size(B, n_idx) > lk::mla_scratch_capacity()) return LK_E_SCRATCH;
+    return from_hip(lk::launch_sparse_mla_static(q_latent, q_rope, kv_latent, kv_rope, cache_seq_stride, cache_rows,
+                                                 idx, B, n_idx, scale, out, stream));
+}
+
 LK_API lk_status lk_profile_next_launch(hipEvent_t start, hipEvent_t stop) {
     if (!start || !stop) return LK_E_NULL;
     lk::armed_events() = lk::LaunchEvents{start, stop};
@@ -258,6 +281,7 @@ LK_API const char *lk_status_string(lk_status s) {
     case LK_E_SHAPE: return "LK_E_SHAPE: sizes are negative or do not fit together";
     case LK_E_UNSUPPORTED: return "LK_E_UNSUPPORTED: outside what this library implements (heads, row length, alignment or grid limits)";
     case LK_E_HIP: return "LK_E_HIP: the HIP runtime rejected a kernel launch";
+    case LK_E_SCRATCH: return "LK_E_SCRATCH: the request needs more workspace than the static scratch buffer (LK_MLA_SCRATCH_BYTES) holds";
     }
     return "unknown lk_status";
 }

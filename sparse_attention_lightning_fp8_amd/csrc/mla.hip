@@ -35,6 +35,9 @@
 // The split writes its unnormalised o with the running max m (base-2 logit units)
 // and sum l to the workspace.
 // Combine kernel: per (b, h), o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+#include <atomic>
+#include <mutex>
+
 #include "lk_device.h"
 
 namespace lk {
@@ -529,6 +532,41 @@ size_t mla_workspace_bytes(int32_t B, int32_t n_idx) {
     return (size_t)B * nsplit * kH * (kDc + 2) * sizeof(float);
 }
 
+// ---- The allocation-free variant's workspace: one static buffer per device, sized for
+// up to kMlaScratchBytes of per-split partials (B * ceil(n_idx / 256) * 128 * 514 floats;
+// 16 rows of 2048 entries take 33.7 MB).  Each device holds its own copy from module
+// load until the process ends.  In host code `scratch` names a host-side stand-in, so
+// the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kMlaScratchBytes = (size_t)LK_MLA_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kMlaScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device `dev` (which must be current), or nullptr if
+// the runtime cannot provide it.
+void *scratch_address(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+        g_scratch_dev[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
+
+size_t mla_scratch_capacity() { return kMlaScratchBytes; }
+
+hipError_t launch_sparse_mla_static(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *kv_lat,
+                                    const uint16_t *kv_rope, int64_t stride, int64_t cap, const int32_t *idx,
+                                    int32_t B, int32_t n_idx, float scale, float *out, hipStream_t stream);
+
 hipError_t launch_sparse_mla(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *kv_lat,
                              const uint16_t *kv_rope, int64_t stride, int64_t cap, const int32_t *idx, int32_t B,
                              int32_t n_idx, float scale, float *out, void *workspace, hipStream_t stream) {
@@ -553,6 +591,19 @@ hipError_t launch_sparse_mla(const uint16_t *q_lat, const uint16_t *q_rope, cons
         if (e != hipSuccess) return e;
     }
     return launch(mla_combine_kernel, dim3((unsigned)(kH / 2 * B)), dim3(256), 0u, stream, a);
+}
+
+// The same launches with the static per-device workspace (see scratch_address); the
+// host checks that the request fits kMlaScratchBytes before calling this.
+hipError_t launch_sparse_mla_static(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *kv_lat,
+                                    const uint16_t *kv_rope, int64_t stride, int64_t cap, const int32_t *idx,
+                                    int32_t B, int32_t n_idx, float scale, float *out, hipStream_t stream) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    void *ws = scratch_address(dev);
+    if (!ws) return hipErrorInvalidSymbol;
+    return launch_sparse_mla(q_lat, q_rope, kv_lat, kv_rope, stride, cap, idx, B, n_idx, scale, out, ws, stream);
 }
 
 }  // namespace lk

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     syms = declared_symbols()
     assert syms == sorted(["lk_quantize_keys", "lk_quantize_queries", "lk_index_score", "lk_topk",
                            "lk_prepare", "lk_decode_score", "lk_sparse_mla_workspace_size",
-                           "lk_sparse_mla_decode", "lk_profile_next_launch", "lk_status_string",
+                           "lk_sparse_mla_decode", "lk_sparse_mla_decode_static", "lk_profile_next_launch",
+                           "lk_status_string",
                            "lk_abi_version"])
 
 
@@ -172,6 +173,23 @@ def test_sparse_mla_validation(lib):
     assert f(A, A, A, A, 16, 16, A, 60000, 25600, 0.1, A, A, 1 << 45, None) == E_UNSUP   # 6e6 blocks
     assert f(A, A, A, A, 16, 16, A, 60000, 256, 0.1, A, A, 0, None) == E_SHAPE   # fits the grid, checks go on
     assert f(None, None, None, None, 16, 16, None, 0, 8, 0.1, None, None, 0, None) == OK
+
+
+def test_sparse_mla_static_validation(lib):
+    f = lib.lk_sparse_mla_decode_static
+    #        qlat qrope kvl kvr stride cap  idx  B   n    scale out stream
+    assert f(A, A, A, A, 16, 17, A, 1, 8, 0.1, A, None) == E_SHAPE              # cap beyond the stride
+    assert f(A, A, A, A, 16, 16, A, 1, -8, 0.1, A, None) == E_SHAPE
+    assert f(None, A, A, A, 16, 16, A, 1, 8, 0.1, A, None) == E_NULL
+    assert f(A, A, A, A, 16, 16, None, 1, 8, 0.1, A, None) == E_NULL
+    assert f(A, A, A, A + 8, 16, 16, A, 1, 8, 0.1, A, None) == E_UNSUP
+    assert f(A, A, A, A, 16, 16, A, 70000, 8, 0.1, A, None) == E_UNSUP          # grid limit
+    # beyond the 64 MiB static buffer (B = 32 rows of 2048 entries need 67.4 MB): refused
+    assert lib.lk_sparse_mla_workspace_size(32, 2048) > (64 << 20)
+    assert lib.lk_sparse_mla_workspace_size(16, 2048) <= (64 << 20)
+    assert f(A, A, A, A, 16384, 16384, A, 32, 2048, 0.1, A, None) == -5         # LK_E_SCRATCH
+    assert lib.lk_status_string(-5).decode().startswith("LK_E_SCRATCH")
+    assert f(None, None, None, None, 16, 16, None, 0, 8, 0.1, None, None) == OK
 
 
 def test_profile_next_launch_validation(lib):
