@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-mla", action="store_true")
     ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the two prefill workloads (for profiling runs); prints no JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     return ap.parse_args()
@@ -224,6 +226,26 @@ def valid_pairs(wl, inp):
             L = min(cap, wl.start_pos + t + 1) if wl.causal else cap
             tot += max(L, 0)
     return tot
+
+
+def time_prefill(api, steps, dev):
+    """Prefill (4096 x 4096 causal) and chunked prefill (2 x 4096 new tokens at
+    12288..16383 against 16384 keys) through lk_prepare, lk_index_score, lk_topk."""
+    import torch
+    res = {}
+    for name in ("prefill_s4096", "chunked_prefill_b2_s4096"):
+        log(f"{name}: setting up")
+        pwl, pinp, pwall, pper = time_workload(api, name, steps, 2, 1, dev)
+        pairs = valid_pairs(pwl, pinp)
+        flops = pairs * FLOP_PER_PAIR
+        tf = flops / (pper["index_score"] * 1e-6) / 1e12
+        res[name] = {"step_ms": pwall / steps * 1e3, "kernel_us": pper,
+                     "valid_pairs": pairs, "score_TFLOPs": tf,
+                     "score_frac_f16_peak": tf / F16_PEAK_TFLOPS, "score_frac_fp8_peak": tf / FP8_PEAK_TFLOPS}
+        log(f"{name}: score {pper['index_score']:.1f} us = {tf:.1f} TFLOP/s")
+        del pinp
+        torch.cuda.empty_cache()
+    return res
 
 
 def time_mla(api, steps, warmup, n_sets, dev):
@@ -410,6 +432,10 @@ def main():
     dev = "cuda:0"
     torch.cuda.init()
 
+    if args.prefill_only:
+        log(json.dumps(time_prefill(api, args.prefill_steps, dev)))
+        return
+
     log("decode_b16_t16384: setting up")
     _, _, uwall, uper = time_workload(api, "decode_b16_t16384", args.steps, args.warmup, args.rotate, dev)
     torch.cuda.empty_cache()
@@ -445,18 +471,7 @@ def main():
         del rinp
         torch.cuda.empty_cache()
     if not args.no_prefill:
-        for name in ("prefill_s4096", "chunked_prefill_b2_s4096"):
-            log(f"{name}: setting up")
-            pwl, pinp, pwall, pper = time_workload(api, name, args.prefill_steps, 2, 1, dev)
-            pairs = valid_pairs(pwl, pinp)
-            flops = pairs * FLOP_PER_PAIR
-            tf = flops / (pper["index_score"] * 1e-6) / 1e12
-            extra[name] = {"step_ms": pwall / args.prefill_steps * 1e3, "kernel_us": pper,
-                           "valid_pairs": pairs, "score_TFLOPs": tf,
-                           "score_frac_f16_peak": tf / F16_PEAK_TFLOPS, "score_frac_fp8_peak": tf / FP8_PEAK_TFLOPS}
-            log(f"{name}: score {pper['index_score']:.1f} us = {tf:.1f} TFLOP/s")
-            del pinp
-            torch.cuda.empty_cache()
+        extra.update(time_prefill(api, args.prefill_steps, dev))
 
     if not args.no_mla:
         log("mla_decode_b16_t16384: setting up")

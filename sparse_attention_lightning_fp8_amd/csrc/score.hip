@@ -405,72 +405,104 @@ __global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeAr
 }
 
 // ------------------------------------------------------------------ prefill (S > 1)
-// A block of 4 waves (one per SIMD) owns 4 consecutive query tokens of one sequence
-// (one per wave) and a slice of 2048 keys, taken as sixteen chunks of 128.  Each
-// chunk is read from HBM once per block, converted to f16 once and kept in LDS, where
-// every wave streams it through the MFMA against its own query held in registers.
-// The chunks are double buffered: the loads of chunk c+1 are issued before chunk c's
-// MFMA work and land in the other LDS buffer after it, and the query is loaded and
-// converted once per slice.  Two blocks share a CU (70 KB of LDS each), so each SIMD
-// runs one wave of each: the two never meet at a barrier, and one block's prologue
-// and chunk hand-overs are covered by the other block's MFMA work.  (With both waves
-// of a SIMD in one block, the issue arbiter's preference for the older wave made the
-// younger one finish each chunk ~40% later while the block waited at the barrier.)
-constexpr int kPreWaves = 4;
+// A block of 8 waves (two per SIMD) owns 8 consecutive query tokens of one sequence (one
+// per wave) and a slice of up to 4096 keys, taken as chunks of 128.  Each chunk is read
+// from HBM once per block, converted to f16 once and kept in LDS, where every wave
+// streams it through the MFMA against its own query held in registers; the chunks are
+// double buffered, so one barrier per chunk publishes the next one.
+//  - Staging layout: thread (wave w, lane l) stages key row 32 (w % 4) + l % 32 of the
+//    chunk, quarter (l / 32) + 2 (w / 4) of the row, and writes it to LDS in the MFMA
+//    B-operand read pattern (rows in lanes 0-31, the next piece of the row in lanes
+//    32-63): the pattern in which the 16-byte LDS accesses are free of bank conflicts.
+//  - The next chunk's loads are issued at the start of a chunk; their conversion and LDS
+//    writes ride in the MFMA stream of the chunk's third tile.
+//  - Chunks valid for the wave's row run as one software pipeline across chunk
+//    boundaries: step g issues the 16 MFMAs of tile g, then the ReLU / weight / head-sum
+//    epilogue of tile g - 1 (two tiles make 64 keys, one per lane after a cross-half
+//    swap), so the VALU epilogue runs in the shadow of the matrix core; chunks that end
+//    past the row's valid length take a plain per-pair path with the mask.
+//  - Work items (sequence, token group, slice) are numbered slice fastest and token
+//    groups from the last (longest causal rows first); the 1-D grid is dispatched to the
+//    8 XCDs round-robin, so block 8p + x (XCD x) takes item 8p + (x + p) % 8, which
+//    gives every XCD every slice equally often instead of pinning slice x to XCD x.
+constexpr int kPreWaves = 8;                          // query tokens per block, one per wave
 constexpr int kPreThreads = 64 * kPreWaves;
-constexpr int kPreChunk = 128;                      // keys per LDS buffer
-constexpr int kPreChunks = 16;                      // chunks per block
-constexpr int kPreSlice = kPreChunk * kPreChunks;   // keys per block
-constexpr int kPreRowBytes = 2 * LK_DIM + 16;       // f16 row + 16 B pad against bank conflicts
-static_assert(kPreThreads == 2 * kPreChunk, "two threads stage each key row");
+constexpr int kPreChunk = 128;                        // keys per LDS buffer
+constexpr int kPreTiles = kPreChunk / 32;
+constexpr int kPreChunks = 32;                        // chunks per slice
+constexpr int kPreSlice = kPreChunk * kPreChunks;     // keys per work item
+constexpr int kPreRowBytes = 2 * LK_DIM + 16;         // f16 row + 16 B pad against bank conflicts
+constexpr int kPreRowGroups = kPreChunk / 32;         // 32-row groups of a chunk
+constexpr int kPrePieces = 2 * kPreWaves / kPreRowGroups;   // pieces each key row is staged in
+constexpr int kPrePieceBytes = LK_DIM / kPrePieces;         // fp8 bytes staged per thread
+constexpr int kPreStageTile = 2;                      // tile whose MFMA stream carries the staging
+static_assert(kPreRowGroups <= kPreWaves && kPrePieces * kPrePieceBytes == LK_DIM && kPrePieceBytes % 16 == 0,
+              "staging map");
+static_assert(kPreChunk <= kPreThreads, "one key scale per thread");
+static_assert(kPreTiles % 2 == 0 && kPreStageTile < kPreTiles, "tile pairs never straddle a chunk");
 
-// One thread's share of a chunk in flight: half a key row (64 fp8 bytes) and, for
+// One thread's share of a chunk in flight: kPrePieceBytes of one key row and, for
 // threads below kPreChunk, one key scale.
 struct ChunkPart {
-    uint4 v[4];
+    uint4 v[kPrePieceBytes / 16];
     float ks;
 };
 
+__device__ __forceinline__ int stage_row() { return 32 * ((threadIdx.x >> 6) % kPreRowGroups) + (threadIdx.x & 31); }
+__device__ __forceinline__ int stage_piece() {
+    return ((threadIdx.x >> 5) & 1) + 2 * ((threadIdx.x >> 6) / kPreRowGroups);
+}
+
+// Rows at or past Lmax (no row of the block needs them) re-read row 0 and are never used.
 __device__ __forceinline__ void load_chunk_part(const uint8_t *__restrict__ kbase, const float *__restrict__ sbase,
                                                 int64_t kc, int64_t Lmax, ChunkPart &p) {
-    const int kr = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const int64_t s = kc + kr;
-    if (s < Lmax) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(kbase + s * LK_DIM + 64 * half);
+    const int64_t s = kc + stage_row();
+    const uint4 *src = reinterpret_cast<const uint4 *>(kbase + (s < Lmax ? s : 0) * LK_DIM +
+                                                       kPrePieceBytes * stage_piece());
 #pragma unroll
-        for (int c = 0; c < 4; c++) p.v[c] = src[c];
-    } else {
-#pragma unroll
-        for (int c = 0; c < 4; c++) p.v[c] = make_uint4(0, 0, 0, 0);
-    }
+    for (int c = 0; c < kPrePieceBytes / 16; c++) p.v[c] = src[c];
     p.ks = (threadIdx.x < kPreChunk && kc + threadIdx.x < Lmax) ? sbase[kc + threadIdx.x] : 0.0f;
 }
 
 __device__ __forceinline__ void store_chunk_part(uint8_t *sk, float *sks, const ChunkPart &p) {
-    const int kr = threadIdx.x >> 1, half = threadIdx.x & 1;
-    half8 *dst = reinterpret_cast<half8 *>(sk + kr * kPreRowBytes + 128 * half);
+    half8 *dst = reinterpret_cast<half8 *>(sk + stage_row() * kPreRowBytes + 2 * kPrePieceBytes * stage_piece());
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
+    for (int c = 0; c < kPrePieceBytes / 16; c++) {
         dst[2 * c] = fp8x8_to_half8(p.v[c].x, p.v[c].y);
         dst[2 * c + 1] = fp8x8_to_half8(p.v[c].z, p.v[c].w);
     }
     if (threadIdx.x < kPreChunk) sks[threadIdx.x] = p.ks;
 }
 
+// Work items of the prefill grid (see above).
+struct PrefillGrid {
+    int nslices, nrg, n_items;
+};
+PrefillGrid prefill_grid(const RowsDev &rows) {
+    PrefillGrid g;
+    g.nslices = (int)((rows.T + kPreSlice - 1) / kPreSlice);
+    g.nrg = (rows.S + kPreWaves - 1) / kPreWaves;
+    g.n_items = g.nslices * g.nrg * rows.B;
+    return g;
+}
+
 __global__ void __launch_bounds__(kPreThreads)
 score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict__ w_eff,
                      const uint8_t *__restrict__ k_cache, const float *__restrict__ k_scale,
-                     int64_t cache_seq_stride, RowsDev rows, float *__restrict__ scores) {
+                     int64_t cache_seq_stride, RowsDev rows, float *__restrict__ scores, PrefillGrid grid) {
     __shared__ __attribute__((aligned(16))) uint8_t sk[2][kPreChunk * kPreRowBytes];
     __shared__ float sks[2][kPreChunk];
+    const int p8 = (int)(blockIdx.x >> 3), x8 = (int)(blockIdx.x & 7);
+    const int item = (p8 << 3) + ((x8 + p8) & 7);
+    if (item >= grid.n_items) return;
+    const int slice = item % grid.nslices;
+    const int rg = grid.nrg - 1 - (item / grid.nslices) % grid.nrg;
+    const int b = item / (grid.nslices * grid.nrg);
     const int lane = __lane_id();
     const int wave = threadIdx.x >> 6;
-    const int b = blockIdx.z;
-    // Row groups in reverse: under a causal mask the longest rows start first, so the
-    // heaviest blocks do not trail at the end of the launch.
-    const int t0 = (gridDim.y - 1 - blockIdx.y) * kPreWaves;
+    const int t0 = rg * kPreWaves;
     const int64_t T = rows.T;
-    const int64_t slice0 = (int64_t)blockIdx.x * kPreSlice;
+    const int64_t slice0 = (int64_t)slice * kPreSlice;
     const int t = t0 + wave;
     const bool has_row = t < rows.S;
     const int64_t L = has_row ? row_len(rows, b, t) : 0;
@@ -486,6 +518,9 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
         for (int64_t s = slice0 + (int64_t)nchunks * kPreChunk + lane; s < slice0 + kPreSlice && s < T; s += 64)
             out[s] = -__builtin_inff();
     if (nchunks == 0) return;
+    // Chunks in which every key is valid for this row: [0, nfull).
+    const int64_t lrow = L - slice0;
+    const int nfull = lrow <= 0 ? 0 : (lrow >= (int64_t)nchunks * kPreChunk ? nchunks : (int)(lrow / kPreChunk));
 
     const uint8_t *kbase = k_cache + (int64_t)b * cache_seq_stride * LK_DIM;
     const float *sbase = k_scale + (int64_t)b * cache_seq_stride;
@@ -499,75 +534,95 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
     store_chunk_part(sk[0], sks[0], part);
     __syncthreads();
     const int r = lane & 31, hh = lane >> 5;
-    for (int c = 0; c < nchunks; c++) {
+    auto mfma_tile = [&](const uint8_t *skc, int j, float16v acc[2]) {
+        const uint8_t *rowbase = skc + (32 * j + r) * kPreRowBytes + 128 * hh;
+        acc[0] = float16v{};
+        acc[1] = float16v{};
+#pragma unroll
+        for (int kk = 0; kk < 8; kk++) {
+            const half8 bk = *reinterpret_cast<const half8 *>(rowbase + 16 * kk);
+#pragma unroll
+            for (int m = 0; m < 2; m++)
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][kk], bk, acc[m], 0, 0, 0);
+        }
+    };
+    // The pipeline over the valid chunks.  Tiles 2i and 2i + 1 of a chunk make 64 keys
+    // (lanes 0-31 and 32-63 after halves_sum_pair); the key scales of a pair are read
+    // into a register right after the previous pair's store.
+    float16v acc[2][2];
+    float p0 = 0.f, ks_pair = 0.f;
+    int64_t s_pair = 0;
+    bool owed = false;                                 // a computed tile still owes its epilogue
+    for (int c = 0; c < nfull; c++) {
         const int64_t kc = slice0 + (int64_t)c * kPreChunk;
         const bool more = c + 1 < nchunks;
         if (more) load_chunk_part(kbase, sbase, kc + kPreChunk, Lmax, part);   // in flight during the MFMA work
         const uint8_t *skc = sk[c & 1];
         const float *sksc = sks[c & 1];
-        if (has_row && kc + kPreChunk <= L) {
-            // Every key of the chunk is valid for this row: a software pipeline in which
-            // the MFMA chain of tile j+1 is issued before the ReLU / weighted-sum epilogue
-            // of tile j, so the VALU epilogue runs in the shadow of the matrix core.
-            const uint8_t *rowbase = skc + r * kPreRowBytes + 128 * hh;
-            auto mfma_tile = [&](int j, float16v acc[2]) {
-                acc[0] = float16v{};
-                acc[1] = float16v{};
+#pragma unroll
+        for (int j = 0; j < kPreTiles; j++) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_tile(skc, j, acc[j & 1]);
+            if (owed) {                                // the epilogue of the previous tile
+                const float pv = relu_weighted_sum(acc[(j + 1) & 1], f);
+                if (j & 1) p0 = pv;                    // the previous tile is the first of a pair
+                else out[s_pair + lane] = halves_sum_pair(p0, pv) * ks_pair;   // s < L <= T
+            }
+            if ((j & 1) == 0) {
+                ks_pair = sksc[32 * j + lane];
+                s_pair = kc + 32 * j;
+            }
+            owed = true;
+            // One scheduling region per step: the tile's 8 operand reads first, then part
+            // of the epilogue while they land, then the MFMA chain interleaved with the
+            // rest of the epilogue (and, in the staging tile, the next chunk's LDS writes).
+            if (j == kPreStageTile) {
+                if (more) store_chunk_part(sk[(c + 1) & 1], sks[(c + 1) & 1], part);
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);       // DS reads
+                __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);      // VALU
 #pragma unroll
                 for (int kk = 0; kk < 8; kk++) {
-                    const half8 bk = *reinterpret_cast<const half8 *>(rowbase + 32 * j * kPreRowBytes + 16 * kk);
-#pragma unroll
-                    for (int m = 0; m < 2; m++)
-                        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][kk], bk, acc[m], 0, 0, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
                 }
-            };
-            float16v acc[2][2];
-            float p[2];
-            mfma_tile(0, acc[0]);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
 #pragma unroll
-            for (int j = 0; j < kPreChunk / 32; j++) {
-                // One scheduling region per stage: the next tile's 8 operand reads first,
-                // then part of this tile's epilogue while they land, then the MFMA chain
-                // interleaved with the rest of the epilogue (two MFMAs, six VALU ops per
-                // K-step).
-                __builtin_amdgcn_sched_barrier(0);
-                if (j + 1 < kPreChunk / 32) mfma_tile(j + 1, acc[(j + 1) & 1]);
-                p[j & 1] = relu_weighted_sum(acc[j & 1], f);
-                if (j & 1) {
-                    const float sum = halves_sum_pair(p[0], p[1]);
-                    const int64_t s = kc + 32 * (j - 1) + lane;
-                    out[s] = sum * sksc[32 * (j - 1) + lane];   // s < L <= T
-                }
-                if (j + 1 < kPreChunk / 32) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);       // the tile's 8 operand reads
-                    __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);      // VALU while they land
-#pragma unroll
-                    for (int kk = 0; kk < 8; kk++) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
-                    }
+                for (int kk = 0; kk < 8; kk++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
-        } else if (has_row) {
-            for (int j = 0; j < kPreChunk / 32; j += 2) {
-                if (kc + 32 * j >= L) {                // rest of this chunk is masked for the row
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    }
+    if (owed) {                                        // the last valid chunk's last tile
+        const float pv = relu_weighted_sum(acc[(kPreTiles - 1) & 1], f);
+        out[s_pair + lane] = halves_sum_pair(p0, pv) * ks_pair;
+    }
+    // Chunks that end past this row's valid length (and rows past S): one tile pair at a
+    // time, masked.  Every wave passes one barrier per chunk in either loop.
+    for (int c = nfull; c < nchunks; c++) {
+        const int64_t kc = slice0 + (int64_t)c * kPreChunk;
+        const bool more = c + 1 < nchunks;
+        if (more) load_chunk_part(kbase, sbase, kc + kPreChunk, Lmax, part);
+        const uint8_t *skc = sk[c & 1];
+        const float *sksc = sks[c & 1];
+        if (has_row) {
+            for (int j = 0; j < kPreTiles; j += 2) {
+                if (kc + 32 * j >= L) {                // the rest of this chunk is masked for the row
                     for (int64_t s = kc + 32 * j + lane; s < kc + kPreChunk && s < T; s += 64) out[s] = -__builtin_inff();
                     break;
                 }
                 float partial[2];
 #pragma unroll
                 for (int jj = 0; jj < 2; jj++) {
-                    const uint8_t *row = skc + (32 * (j + jj) + r) * kPreRowBytes + 128 * hh;
-                    float16v acc[2] = {};
-#pragma unroll
-                    for (int kk = 0; kk < 8; kk++) {
-                        const half8 bk = *reinterpret_cast<const half8 *>(row + 16 * kk);
-#pragma unroll
-                        for (int m = 0; m < 2; m++)
-                            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][kk], bk, acc[m], 0, 0, 0);
-                    }
-                    partial[jj] = relu_weighted_sum(acc, f);
+                    float16v a2[2];
+                    mfma_tile(skc, j + jj, a2);
+                    partial[jj] = relu_weighted_sum(a2, f);
                 }
                 const float sum = halves_sum_pair(partial[0], partial[1]);
                 const int64_t s = kc + 32 * j + lane;
@@ -614,7 +669,10 @@ hipError_t launch_decode_grid(const DecodeArgs &a, hipStream_t stream) {
 bool index_score_grid_fits(const RowsDev &rows) {
     if (rows.B > 65535) return false;
     if (rows.S == 1) return (rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock <= 0x7FFFFFFF;
-    return (rows.S + kPreWaves - 1) / kPreWaves <= 65535 && (rows.T + kPreSlice - 1) / kPreSlice <= 0x7FFFFFFF;
+    // prefill: one block per (sequence, 8-token group, 4096-key slice), rounded up to 8
+    const int64_t items = (int64_t)rows.B * ((rows.S + kPreWaves - 1) / kPreWaves) *
+                          ((rows.T + kPreSlice - 1) / kPreSlice);
+    return (items + 7) / 8 * 8 <= 0x7FFFFFFF;
 }
 
 hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
@@ -631,10 +689,10 @@ hipError_t launch_index_score(const uint8_t *q_fp8, const float *w_eff, const ui
         a.scores = scores;
         return launch_decode_grid<false>(a, stream);
     } else {
-        dim3 grid((unsigned)((rows.T + kPreSlice - 1) / kPreSlice), (unsigned)((rows.S + kPreWaves - 1) / kPreWaves),
-                  (unsigned)rows.B);
-        return launch(score_prefill_kernel, grid, dim3(kPreThreads), 0u, stream, q_fp8, w_eff, k_cache,
-                      k_scale, cache_seq_stride, rows, scores);
+        const PrefillGrid g = prefill_grid(rows);
+        const unsigned blocks = (unsigned)((g.n_items + 7) / 8 * 8);
+        return launch(score_prefill_kernel, dim3(blocks), dim3(kPreThreads), 0u, stream, q_fp8, w_eff, k_cache,
+                      k_scale, cache_seq_stride, rows, scores, g);
     }
 }
 
