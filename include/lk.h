@@ -167,7 +167,8 @@ LK_API lk_status lk_prepare(const uint16_t *x, int64_t n_seq, int64_t n_rows, in
  * the mask are applied in registers; each score is written once.
  * Requires heads == 64 (else LK_E_UNSUPPORTED), T <= cache_seq_stride,
  * q_fp8 and k_cache 16-byte aligned, w_eff 16-byte aligned.  LK_E_UNSUPPORTED past
- * the launch grid limits: B > 65535, or (S > 1) ceil(S / 4) > 65535.
+ * the launch grid limits: B > 65535, or (S > 1) B * ceil(S / 8) * ceil(T / 4096)
+ * blocks above 2^31 - 8.
  */
 LK_API lk_status lk_index_score(const uint8_t *q_fp8, const float *w_eff, int32_t heads,
                                 const uint8_t *k_cache, const float *k_scale,

@@ -30,15 +30,27 @@ def build() -> str:
     return _LIB
 
 
+def build_sanitized(out_path: str) -> str:
+    """The same library built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any report aborts), for the CPU sanitizer tests.  Loading it needs gcc's libasan
+    preloaded; ``LK_ORACLE_LIB=<out_path>`` makes ``lib()`` load it."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-fPIC", "-shared",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           _SRC, "-o", out_path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
 _lib = None
 
 
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        path = os.environ.get("LK_ORACLE_LIB", _LIB)
+        if path == _LIB and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         L.lko_e4m3_decode.argtypes = [ctypes.c_uint8]

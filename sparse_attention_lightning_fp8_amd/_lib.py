@@ -7,7 +7,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblk.so")
+# The in-tree build; LK_LIB_PATH names another build of the same library (the CPU
+# sanitizer tests load a host-instrumented copy through it).
+LIB_PATH = os.environ.get("LK_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblk.so")
 
 LK_OK = 0
 STATUS_NAMES = {0: "LK_OK", -1: "LK_E_NULL", -2: "LK_E_SHAPE", -3: "LK_E_UNSUPPORTED", -4: "LK_E_HIP",

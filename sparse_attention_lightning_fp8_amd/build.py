@@ -55,5 +55,34 @@ def build() -> str:
     return LIB_PATH
 
 
+# Host-side AddressSanitizer / UndefinedBehaviorSanitizer build (device code as
+# usual): every sanitizer flag applies to the host pass only.  Used by the CPU tests of
+# the argument validation; loading it needs clang's ASan runtime preloaded.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """liblk.so with the host code instrumented, built into out_dir; returns its path."""
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(src: str) -> str:
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *HOST_SANITIZE, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    out = os.path.join(out_dir, "liblk.so")
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *HOST_SANITIZE, "-shared-libsan",
+                        *objs, "-o", out], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     print(build())

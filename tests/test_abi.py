@@ -114,9 +114,9 @@ def test_index_score_validation(lib):
     assert f(A, A + 4, 64, A, A, 16, rows(), A, None) == E_UNSUP
     assert f(A, A, 64, A, A, 16, rows(seq_len=A + 1), A, None) == E_UNSUP
     assert f(A, A, 64, A, A, 70000, rows(B=70000, T=16), A, None) == E_UNSUP  # grid limit
-    # prefill grid: one block row per four query tokens, at most 65535
-    assert f(A, A, 64, A, A, 16, rows(S=4 * 65535 + 1, T=16), A + 8, None) == E_UNSUP   # alignment first
-    assert f(A, A, 64, A, A, 16, rows(S=4 * 65535, T=16, seq_len=A + 2), A, None) == E_UNSUP
+    # prefill grid: one block per (sequence, 8-token group, 4096-key slice), at most 2^31 - 1
+    assert f(A, A, 64, A, A, 16, rows(B=65535, S=1 << 27, T=16), A, None) == E_UNSUP
+    assert f(A, A, 64, A, A, 16, rows(S=4 * 65535, T=16, seq_len=A + 2), A, None) == E_UNSUP   # misaligned
     assert f(None, None, 64, None, None, 16, rows(B=0), None, None) == OK
     assert f(None, None, 64, None, None, 16, rows(T=0), None, None) == OK
 

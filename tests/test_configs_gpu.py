@@ -14,13 +14,25 @@ from tests._parity import OracleCase, compare_scores, compare_topk, gpu_pipeline
 
 pytestmark = pytest.mark.gpu
 
-# (workload, rows to check as (b, t))
+# (workload, rows to check as (b, t)).  Prefill rows cover every position of an 8-token
+# block (the prefill kernel's token group), both sides of 128-key chunk and 2048/4096-key
+# slice edges, rows whose causal diagonal ends mid-chunk, and a spread over token groups.
+def _prefill_rows(S, seqs, extra, group_step):
+    ts = set(range(8)) | set(range(S - 8, S)) | set(extra)
+    ts |= {8 * g + g % 8 for g in range(0, S // 8, group_step)}
+    return [(b, t) for b in seqs for t in sorted(x for x in ts if 0 <= x < S)]
+
+
 SAMPLES = {
     "decode_b1_t1001": [(0, 0)],
-    "decode_b16_t16384": [(0, 0), (7, 0), (15, 0)],
+    "decode_b16_t16384": [(b, 0) for b in range(16)],
     "ragged_decode_b64": "ragged",
-    "prefill_s4096": [(0, t) for t in (0, 1, 7, 8, 255, 256, 1000, 2046, 2047, 2048, 3001, 4095)],
-    "chunked_prefill_b2_s4096": [(0, 0), (0, 777), (0, 4095), (1, 1), (1, 2048), (1, 4094)],
+    # causal 4096 x 4096: row t has t + 1 keys
+    "prefill_s4096": _prefill_rows(4096, [0], [126, 127, 128, 129, 255, 256, 1000, 2046, 2047, 2048, 2049,
+                                                3001, 4094], 11),
+    # 4096 new tokens at 12288..16383: row t has 12289 + t keys; slice edges at keys
+    # 4096, 8192, 12288; chunk-aligned lengths at t = 127, 2047, 3967
+    "chunked_prefill_b2_s4096": _prefill_rows(4096, [0, 1], [126, 127, 128, 1023, 2046, 2047, 2048, 3967], 23),
 }
 
 
@@ -28,9 +40,17 @@ def _rows_for(name, inp):
     s = SAMPLES[name]
     if s == "ragged":
         lens = inp.lens.numpy()
-        pick = {int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 40, 63}
+        order = np.argsort(lens, kind="stable")
+        pick = {int(order[0]), int(order[1]), int(order[-1]), int(order[-2])} | set(range(0, 64, 4))
         return [(b, 0) for b in sorted(pick)]
     return s
+
+
+def test_sample_sizes():
+    """At least 64 oracle rows for each prefill workload and every decode row of B16."""
+    assert len(SAMPLES["prefill_s4096"]) >= 64
+    assert len(SAMPLES["chunked_prefill_b2_s4096"]) >= 64
+    assert len({b for b, _ in SAMPLES["chunked_prefill_b2_s4096"]}) == 2
 
 
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
@@ -78,7 +98,7 @@ def test_workload_end_to_end(name):
     # every row of the GPU output satisfies the mask and top-k structure
     B, S, T = scores.shape
     for b in range(B):
-        for t in range(0, S, max(1, S // 64)):
+        for t in range(0, S, 1 if S <= 64 else 3):
             L = oc.row_len(b, t)
             assert np.all(np.isneginf(scores[b, t, L:])) and np.all(np.isfinite(scores[b, t, :L]))
             kr = min(wl.k, L)
