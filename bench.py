@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the two prefill workloads (for profiling runs); prints no JSON line")
+    ap.add_argument("--floors-only", action="store_true",
+                    help="only the probe-kernel floors (empty launch, plain read); prints no JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     return ap.parse_args()
@@ -344,6 +346,50 @@ def cpu_baseline(wl_name):
                       f"{keys} key scores, top-{wl.k} each), single-threaded, {dt:.2f} s"}
 
 
+def probe_floors(dev, launches=200):
+    """Floors measured with the library's probe kernels: the duration of an empty kernel
+    between its own start and end events (and the wall time per launch back to back),
+    and a plain read of the decode workload's 32 MiB key cache, 16 rotated copies (so
+    the 256 MB last-level cache cannot serve them), at 1024 and 512 blocks."""
+    import torch
+    from sparse_attention_lightning_fp8_amd import _lib
+    lib = _lib.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    arm = lib.lk_profile_next_launch
+    res = {}
+    ev = make_event_pairs(launches, 1)
+    for i in range(20):
+        lib.lk_probe_empty(256, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(launches):
+        lib.lk_probe_empty(256, stream)
+    torch.cuda.synchronize()
+    res["empty_kernel_wall_us_per_launch"] = (time.perf_counter() - t0) / launches * 1e6
+    for i in range(launches):
+        arm(ev[i][0][0].cuda_event, ev[i][0][1].cuda_event)
+        lib.lk_probe_empty(256, stream)
+    torch.cuda.synchronize()
+    res["empty_kernel_event_us"] = sum(e[0][0].elapsed_time(e[0][1]) for e in ev) / launches * 1e3
+    n = 16384 * 16 * 128                                   # the key cache of decode_b16_t16384
+    bufs = [torch.ones(n // 4, dtype=torch.int32, device=dev) for _ in range(16)]
+    for blocks in (1024, 512):
+        sink = torch.empty(blocks * 4, dtype=torch.int32, device=dev)
+        for i in range(20):
+            lib.lk_probe_read(bufs[i % 16].data_ptr(), n, sink.data_ptr(), blocks, stream)
+        torch.cuda.synchronize()
+        for i in range(launches):
+            arm(ev[i][0][0].cuda_event, ev[i][0][1].cuda_event)
+            lib.lk_probe_read(bufs[i % 16].data_ptr(), n, sink.data_ptr(), blocks, stream)
+        torch.cuda.synchronize()
+        us = sum(e[0][0].elapsed_time(e[0][1]) for e in ev) / launches * 1e3
+        res[f"read_32MiB_{blocks}_blocks_us"] = us
+        res[f"read_32MiB_{blocks}_blocks_GBps"] = n / (us * 1e-6) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def empirical_ceilings(dev):
     """Second denominators measured with library kernels (PyTorch's own): a 32 MiB
     device copy (bytes read plus bytes written) and a dense f16 GEMM (8192^3 through
@@ -435,6 +481,9 @@ def main():
     if args.prefill_only:
         log(json.dumps(time_prefill(api, args.prefill_steps, dev)))
         return
+    if args.floors_only:
+        log(json.dumps(probe_floors(dev)))
+        return
 
     log("decode_b16_t16384: setting up")
     _, _, uwall, uper = time_workload(api, "decode_b16_t16384", args.steps, args.warmup, args.rotate, dev)
@@ -479,6 +528,9 @@ def main():
         log(f"sparse MLA decode: {extra['mla_decode_b16_t16384']['call_us']:.1f} us per call")
         torch.cuda.empty_cache()
 
+    log("floors (probe kernels): running")
+    extra["floors"] = probe_floors(dev)
+    log(f"floors: {extra['floors']}")
     log("empirical ceilings: running")
     extra["empirical_ceilings"] = empirical_ceilings(dev)
     log(f"empirical ceilings: {extra['empirical_ceilings']}")

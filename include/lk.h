@@ -269,6 +269,27 @@ LK_API lk_status lk_sparse_mla_decode_static(const uint16_t *q_latent, const uin
                                              hipStream_t stream);
 
 /*
+ * Measurement aids, outside the indexer computation (they serve the benchmark's
+ * floors and the accuracy test of the fp8 matrix core; nothing in the hot path calls
+ * them):
+ *   lk_probe_empty: an empty kernel of `blocks` 64-thread blocks (the fixed cost of
+ *     one launch).  LK_E_SHAPE unless 1 <= blocks <= 2^31 / 64.
+ *   lk_probe_read: `blocks` 256-thread blocks read the `bytes` at src once (16-byte
+ *     loads, contiguous span per block) and write one word per wave to
+ *     sink[blocks * 4] (DEVICE).  bytes must be a multiple of 16 (else LK_E_SHAPE).
+ *   lk_probe_fp8_mfma_score: lk_index_score for decode rows (S == 1) with the
+ *     contraction on the fp8 MFMA (v_mfma_f32_16x16x32_fp8_fp8) instead of exactly
+ *     converted f16 operands; arguments as lk_index_score (heads fixed at 64),
+ *     LK_E_SHAPE if S > 1.  q_fp8 and k_cache 8-byte aligned.
+ */
+LK_API lk_status lk_probe_empty(int32_t blocks, hipStream_t stream);
+LK_API lk_status lk_probe_read(const void *src, size_t bytes, uint32_t *sink, int32_t blocks,
+                               hipStream_t stream);
+LK_API lk_status lk_probe_fp8_mfma_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
+                                         const float *k_scale, int64_t cache_seq_stride, const lk_rows *rows,
+                                         float *scores, hipStream_t stream);
+
+/*
  * Profiling aid, outside the indexer computation: arm two HIP events for the next
  * kernel that the calling thread launches through an lk_* entry point.  The runtime
  * records `start` when that kernel begins executing and `stop` when it ends

@@ -41,6 +41,9 @@ SIGNATURES = {
                                             ctypes.c_size_t, _p]),
     "lk_sparse_mla_decode_static": (ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _p, _i32, _i32, ctypes.c_float,
                                                    _p, _p]),
+    "lk_probe_empty": (ctypes.c_int, [_i32, _p]),
+    "lk_probe_read": (ctypes.c_int, [_p, ctypes.c_size_t, _p, _i32, _p]),
+    "lk_probe_fp8_mfma_score": (ctypes.c_int, [_p, _p, _p, _p, _i64, ctypes.POINTER(LkRows), _p, _p]),
     "lk_profile_next_launch": (ctypes.c_int, [_p, _p]),
     "lk_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lk_abi_version": (_i32, []),

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "liblk.so")
-SOURCES = ["quantize.hip", "score.hip", "topk.hip", "mla.hip", "lk_api.hip"]
+SOURCES = ["quantize.hip", "score.hip", "topk.hip", "mla.hip", "probe.hip", "lk_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -26,6 +26,7 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
 # contract), so ReLU may compile to a single v_max without IEEE NaN canonicalization;
 # their MFMA accumulators stay in VGPRs, which the epilogue reads directly.
 FILE_FLAGS = {"score.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "probe.hip": ["-fno-honor-nans"],
               "mla.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

@@ -15,6 +15,11 @@ hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t
                                float *k_scale, int64_t cache_seq_stride, const RowsDev &rows, float *scores,
                                uint8_t *q_fp8_out, float *w_eff_out, const float *rope_cos,
                                const float *rope_sin, hipStream_t stream);
+hipError_t launch_probe_empty(int32_t blocks, hipStream_t stream);
+hipError_t launch_probe_read(const void *src, uint64_t bytes, uint32_t *sink, int32_t blocks, hipStream_t stream);
+hipError_t launch_probe_fp8_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
+                                  const float *k_scale, int64_t cache_seq_stride, const RowsDev &rows, float *scores,
+                                  hipStream_t stream);
 size_t mla_workspace_bytes(int32_t B, int32_t n_idx);
 size_t mla_scratch_capacity();
 hipError_t launch_sparse_mla_static(const uint16_t *q_lat, const uint16_t *q_rope, const uint16_t *kv_lat,
@@ -266,6 +271,38 @@ LK_API lk_status lk_sparse_mla_decode_static(const uint16_t *q_latent, const uin
     if (lk_sparse_mla_workspace_size(B, n_idx) > lk::mla_scratch_capacity()) return LK_E_SCRATCH;
     return from_hip(lk::launch_sparse_mla_static(q_latent, q_rope, kv_latent, kv_rope, cache_seq_stride, cache_rows,
                                                  idx, B, n_idx, scale, out, stream));
+}
+
+LK_API lk_status lk_probe_empty(int32_t blocks, hipStream_t stream) {
+    DisarmOnExit disarm;
+    if (blocks < 1 || blocks > kMaxGridX / 64) return LK_E_SHAPE;
+    return from_hip(lk::launch_probe_empty(blocks, stream));
+}
+
+LK_API lk_status lk_probe_read(const void *src, size_t bytes, uint32_t *sink, int32_t blocks, hipStream_t stream) {
+    DisarmOnExit disarm;
+    if (blocks < 1 || blocks > kMaxGridX / 256 || bytes % 16 != 0) return LK_E_SHAPE;
+    if (bytes == 0) return LK_OK;
+    if (!src || !sink) return LK_E_NULL;
+    if (!aligned(src, 16) || !aligned(sink, 4)) return LK_E_UNSUPPORTED;
+    return from_hip(lk::launch_probe_read(src, (uint64_t)bytes, sink, blocks, stream));
+}
+
+LK_API lk_status lk_probe_fp8_mfma_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
+                                         const float *k_scale, int64_t cache_seq_stride, const lk_rows *rows,
+                                         float *scores, hipStream_t stream) {
+    DisarmOnExit disarm;
+    lk_status st = check_rows(rows);
+    if (st != LK_OK) return st;
+    if (cache_seq_stride < 0 || rows->T > cache_seq_stride || rows->S > 1) return LK_E_SHAPE;
+    if (rows->B == 0 || rows->S == 0 || rows->T == 0) return LK_OK;
+    if (!q_fp8 || !w_eff || !k_cache || !k_scale || !scores) return LK_E_NULL;
+    if (!aligned(q_fp8, 8) || !aligned(k_cache, 8) || !aligned(w_eff, 4) || !aligned(k_scale, 4) ||
+        !aligned(scores, 4) || !aligned(rows->seq_len, 4))
+        return LK_E_UNSUPPORTED;
+    if (rows->B > kMaxGridYZ || (rows->T + 63) / 64 > kMaxGridX) return LK_E_UNSUPPORTED;
+    return from_hip(lk::launch_probe_fp8_score(q_fp8, w_eff, k_cache, k_scale, cache_seq_stride, to_dev(*rows),
+                                               scores, stream));
 }
 
 LK_API lk_status lk_profile_next_launch(hipEvent_t start, hipEvent_t stop) {

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     assert syms == sorted(["lk_quantize_keys", "lk_quantize_queries", "lk_index_score", "lk_topk",
                            "lk_prepare", "lk_decode_score", "lk_sparse_mla_workspace_size",
                            "lk_sparse_mla_decode", "lk_sparse_mla_decode_static", "lk_profile_next_launch",
-                           "lk_status_string",
+                           "lk_probe_empty", "lk_probe_read", "lk_probe_fp8_mfma_score", "lk_status_string",
                            "lk_abi_version"])
 
 
@@ -190,6 +190,21 @@ def test_sparse_mla_static_validation(lib):
     assert f(A, A, A, A, 16384, 16384, A, 32, 2048, 0.1, A, None) == -5         # LK_E_SCRATCH
     assert lib.lk_status_string(-5).decode().startswith("LK_E_SCRATCH")
     assert f(None, None, None, None, 16, 16, None, 0, 8, 0.1, None, None) == OK
+
+
+def test_probe_validation(lib):
+    assert lib.lk_probe_empty(0, None) == E_SHAPE
+    assert lib.lk_probe_read(A, 24, A, 4, None) == E_SHAPE                   # not a multiple of 16
+    assert lib.lk_probe_read(A, 32, A, 0, None) == E_SHAPE
+    assert lib.lk_probe_read(None, 32, A, 4, None) == E_NULL
+    assert lib.lk_probe_read(A + 8, 32, A, 4, None) == E_UNSUP
+    assert lib.lk_probe_read(None, 0, None, 4, None) == OK
+    f = lib.lk_probe_fp8_mfma_score
+    assert f(A, A, A, A, 16, rows(S=2), A, None) == E_SHAPE                  # decode rows only
+    assert f(A, A, A, A, 16, rows(T=17), A, None) == E_SHAPE
+    assert f(None, A, A, A, 16, rows(), A, None) == E_NULL
+    assert f(A + 4, A, A, A, 16, rows(), A, None) == E_UNSUP
+    assert f(None, None, None, None, 16, rows(B=0), None, None) == OK
 
 
 def test_profile_next_launch_validation(lib):
