@@ -308,21 +308,28 @@ def time_mla(api, steps, warmup, n_sets, dev):
 
 
 # ---------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(wl_name):
-    """The oracle, single-threaded, on the same decode step (all 16 rows): key write of the
-    new rows, query quantize + fold, scores against every cached key, sort-based top-k.
-    Its cache prefix is quantized by the oracle itself beforehand (untimed)."""
+def cpu_baseline(wl_name, seconds=5.0):
+    """The oracle (plain single-threaded C through ctypes, which releases the GIL during
+    each call) on the same decode step: key write of the new rows, query quantize +
+    fold, scores against every cached key, sort-based top-k.  Timed twice on whole steps
+    repeated for about `seconds` each: on one core, and with the step's rows split over
+    P = min(cpu count, 16) threads, one row range each.  Then the oracle's prefill rate
+    (GFLOP/s, 16,384 flop per scored pair) on a sample of chunked-prefill rows over the
+    same P threads.  The cache prefix is quantized by the oracle beforehand (untimed)."""
+    import concurrent.futures
     import numpy as np
     from oracle import oracle as O
     from sparse_attention_lightning_fp8_amd import workloads as W
     wl = W.WORKLOADS[wl_name]
     inp = W.make_inputs(wl, seed=0)
+    P = max(1, min(os.cpu_count() or 1, 16))
     prefix = []
     for b in range(wl.B):
         p0 = int(inp.positions[b])
         prefix.append(O.quantize_rows(W.bf16_bits(inp.k[b, :p0])))
-    def step():
-        for b in range(wl.B):
+
+    def rows_step(bs):
+        for b in bs:
             p0 = int(inp.positions[b])
             kn, ksn = O.quantize_rows(W.bf16_bits(inp.k[b, p0:p0 + wl.S]))
             k8 = np.concatenate([prefix[b][0], kn])
@@ -333,17 +340,45 @@ def cpu_baseline(wl_name):
                 L = O.valid_len(wl.T, -1, wl.causal, wl.start_pos, t)
                 s = O.score_row(q8, w_eff, k8, ks, wl.T, L)
                 O.topk(s, L, wl.k)
-    # whole steps, repeated until about 10 s of CPU work (at most 30 steps)
-    t0 = time.perf_counter()
-    reps = 0
-    while reps < 30 and (reps == 0 or time.perf_counter() - t0 < 10.0):
-        step()
-        reps += 1
-    dt = time.perf_counter() - t0
+
+    def timed(step):
+        t0 = time.perf_counter()
+        reps = 0
+        while reps < 30 and (reps == 0 or time.perf_counter() - t0 < seconds):
+            step()
+            reps += 1
+        return reps, time.perf_counter() - t0
+
     keys = wl.B * wl.S * wl.T
-    return {"value": keys * reps / dt, "unit": "keys/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full {wl_name} steps (B={wl.B}, T={wl.T}: key write, query quantize, "
-                      f"{keys} key scores, top-{wl.k} each), single-threaded, {dt:.2f} s"}
+    reps1, dt1 = timed(lambda: rows_step(range(wl.B)))
+    shards = [list(range(wl.B))[i::P] for i in range(P)]
+    shards = [s_ for s_ in shards if s_]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(shards)) as ex:
+        repsP, dtP = timed(lambda: list(ex.map(rows_step, shards)))
+        # prefill: oracle scores of chunked_prefill_b2_s4096 rows (keys written by the oracle)
+        pw = W.WORKLOADS["chunked_prefill_b2_s4096"]
+        pinp = W.make_inputs(pw, seed=0)
+        pk8, pks = O.quantize_rows(W.bf16_bits(pinp.k[0]))
+        sample = list(range(0, pw.S, pw.S // (2 * P)))[:2 * P]
+
+        def prow(t):
+            q8, qs = O.quantize_rows(W.bf16_bits(pinp.q[0, t]))
+            w_eff = O.fold_weights(pinp.w[0, t].numpy(), qs)
+            L = O.valid_len(pw.T, -1, pw.causal, pw.start_pos, t)
+            O.score_row(q8, w_eff, pk8, pks, pw.T, L)
+            return L
+
+        t0 = time.perf_counter()
+        pairs = sum(ex.map(prow, sample))
+        dtp = time.perf_counter() - t0
+    return {"value": keys * repsP / dtP, "unit": "keys/s", "cores": len(shards), "kind": "oracle",
+            "sample": f"{repsP} full {wl_name} steps (B={wl.B}, T={wl.T}: key write, query quantize, {keys} key "
+                      f"scores, top-{wl.k} each) with the rows split over {len(shards)} threads, {dtP:.2f} s",
+            "single_core_keys_per_s": keys * reps1 / dt1,
+            "single_core_sample": f"{reps1} steps on one thread, {dt1:.2f} s",
+            "prefill_GFLOPs": pairs * FLOP_PER_PAIR / dtp / 1e9,
+            "prefill_sample": f"{len(sample)} rows of chunked_prefill_b2_s4096 (sequence 0, {pairs} scored pairs) "
+                              f"over {len(shards)} threads, {dtp:.2f} s"}
 
 
 def probe_floors(dev, launches=200):
@@ -539,7 +574,8 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle): running")
         cpu = cpu_baseline("decode_b16_t16384")
-        log(f"cpu baseline: {cpu['value']:.3e} keys/s")
+        log(f"cpu baseline: {cpu['value']:.3e} keys/s on {cpu['cores']} threads, "
+            f"{cpu['single_core_keys_per_s']:.3e} on one; prefill {cpu['prefill_GFLOPs']:.2f} GFLOP/s")
 
     out = {
         "metric": METRIC, "value": value, "unit": "keys/s", "n_gpus": 1,
