@@ -88,9 +88,12 @@ __device__ __forceinline__ float relu_weighted_sum(const float16v acc[2], const 
     return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
-// Scores of one 32-key tile whose B operand (this lane's 64 bytes of key l % 32) is `kv`.
-__device__ __forceinline__ float score_tile(const uint4 kv[4], const QueryFrag &f) {
-    float16v acc[2] = {};
+// The 16 MFMAs of one 32-key tile whose B operand (this lane's 64 bytes of key l % 32)
+// is `kv`: acc[m] holds heads 32m .. 32m + 31 against the tile's keys.  Each fp8 K-step
+// is converted to f16 right before its two MFMAs.
+__device__ __forceinline__ void mfma_tile(const uint4 (&kv)[4], const QueryFrag &f, float16v (&acc)[2]) {
+    acc[0] = float16v{};
+    acc[1] = float16v{};
 #pragma unroll
     for (int c = 0; c < 4; c++) {
         const half8 b0 = fp8x8_to_half8(kv[c].x, kv[c].y);
@@ -101,30 +104,94 @@ __device__ __forceinline__ float score_tile(const uint4 kv[4], const QueryFrag &
             acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[m][2 * c + 1], b1, acc[m], 0, 0, 0);
         }
     }
-    return relu_weighted_sum(acc, f);
+}
+
+// One wave's kTiles tiles of 32 consecutive keys from key0, as a software pipeline:
+// step j issues the MFMAs of tile j + 1 interleaved with the ReLU / weight / head-sum
+// epilogue of tile j, so with one or two waves per SIMD the matrix core and the VALU
+// still overlap.  Tiles 0 .. kFly - 1 must be in flight already; step j issues tile
+// j + kFly (load_tile(j + kFly)), kFly steps before it is needed.  Two tiles make 64
+// keys, one per lane after a cross-half swap (lanes 0-31: tile 2p, lanes 32-63: tile
+// 2p + 1 -> key key0 + 64 p + lane), scaled by ks[p] and stored (-inf past the valid
+// prefix L, nothing past T).  kNewKey: the lane holding key `pn` (-1: none) takes its
+// operand from `nk` (LDS: the new key's 128 codes, 64 bytes per lane half) in place of
+// the row it loaded (a select, so the steps stay free of branches).
+template <int kTiles, int kFly, bool kNewKey, typename LoadTile>
+__device__ __forceinline__ void pipelined_tiles(uint4 (&kv)[kTiles][4], LoadTile load_tile, const QueryFrag &f,
+                                                const float (&ks)[kTiles / 2], int64_t key0, int64_t pn,
+                                                const uint4 *nk, int64_t T, int64_t L, float *out) {
+    static_assert(kTiles % 2 == 0 && kFly >= 1 && kFly <= kTiles, "tile schedule");
+    const int lane = __lane_id(), r = lane & 31;
+    auto start_tile = [&](int j, float16v (&acc)[2]) {
+        if constexpr (kNewKey) {
+            const bool mine = key0 + 32 * j + r == pn;
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const uint4 n = nk[4 * (lane >> 5) + c];
+                kv[j][c].x = mine ? n.x : kv[j][c].x;
+                kv[j][c].y = mine ? n.y : kv[j][c].y;
+                kv[j][c].z = mine ? n.z : kv[j][c].z;
+                kv[j][c].w = mine ? n.w : kv[j][c].w;
+            }
+        }
+        mfma_tile(kv[j], f, acc);
+    };
+    float16v acc[2][2];
+    float part[2];
+    start_tile(0, acc[0]);
+#pragma unroll
+    for (int j = 0; j < kTiles; j++) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + kFly < kTiles) load_tile(j + kFly);
+        if (j + 1 < kTiles) start_tile(j + 1, acc[(j + 1) & 1]);
+        part[j & 1] = relu_weighted_sum(acc[j & 1], f);
+        if (j & 1) {
+            const float sum = halves_sum_pair(part[0], part[1]);
+            const int64_t s = key0 + 64 * (j / 2) + lane;
+            if (s < T) out[s] = s < L ? sum * ks[j / 2] : -__builtin_inff();
+        }
+        if (j + 1 < kTiles) {
+#pragma unroll
+            for (int c = 0; c < 8; c++) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // conversions of the next K-step
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // its two MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // epilogue VALU of the current tile
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // ------------------------------------------------------------------ decode (S == 1)
-// One wave scores 128 consecutive keys (4 tiles of 32) of one query row; a block of
-// kDecWaves waves covers kDecKeysPerBlock keys of that row.  Each lane loads its
-// 4 x 64 bytes of K straight into the B-operand registers (keys are read exactly
-// once, so staging K in LDS brings no reuse).  The query (8 KB as e4m3fn) and its
-// weights (256 B) are needed by every wave: the block fetches them once into LDS and
-// each wave takes its A fragments from there.
-// Order of work: the query loads, then every K load of the wave (16 KB in flight),
-// then the query staging while K streams in, then the tiles in arrival order.
+// Work is cut into items of kDecKeysPerBlock (1024) consecutive keys of one query row.
+// Three kernels cover them:
+//  - decode_kernel (the fused step, one block per item): loader waves stream the
+//    item's keys into LDS while compute waves prepare the query;
+//  - decode_pipe_kernel (lk_index_score with a prepared query, one block per item):
+//    four waves with K in registers;
+//  - decode_persistent_kernel (both, when the items outnumber what the chip runs at
+//    once): one block per compute unit walks a range of items with decode_item.
+// In decode_item, one wave scores 128 consecutive keys (4 tiles of 32) and a block of
+// kDecWaves waves covers the item.  Each lane loads its 4 x 64 bytes of K straight
+// into the B-operand registers (keys are read exactly once, so staging K in LDS brings
+// no reuse).  The query (8 KB as e4m3fn) and its weights (256 B) are needed by every
+// wave: the block fetches them once into LDS and each wave takes its A fragments from
+// there.  Order of work: the query loads, then the first kDecFly K tiles of the wave,
+// then the query staging while K streams in, then the tiles through pipelined_tiles,
+// which requests the rest of K as it goes.
 //
-// The fused variant (lk_decode_score) starts from the bf16 query, the raw weights
-// and the new key of the decode step: each block quantizes the row's 64 query heads
-// itself (8 lanes per head, the same arithmetic as lk_quantize_queries) while its K
-// loads are in flight, and the block holding key L-1 (the new token's slot) also
-// rotates and quantizes the new key, writes it to the cache, and hands it to the
-// lanes that score it in place of the stale cache row they loaded.
+// The fused kernels (lk_decode_score) start from the bf16 query, the raw weights and
+// the new key of the decode step: each block quantizes the row's 64 query heads itself
+// (8 lanes per head, the same arithmetic as lk_quantize_queries), and the block
+// holding key L-1 (the new token's slot) also rotates and quantizes the new key,
+// writes it to the cache, and hands it to the lanes that score it in place of the
+// stale cache row they loaded.
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecTiles = 4;                       // 32-key tiles per wave
 constexpr int kDecKeysPerWave = 32 * kDecTiles;    // 128
 constexpr int kDecKeysPerBlock = kDecKeysPerWave * kDecWaves;
+constexpr int kDecFly = kDecTiles / 2;             // tiles in flight ahead of the MFMA stream
 constexpr int kQPitch = LK_DIM + 16;               // LDS row pitch of the staged query (spreads banks)
 static_assert(LK_HEADS * LK_DIM / 16 == kDecThreads, "one 16-byte query piece per thread");
 static_assert(LK_HEADS * 8 == kDecThreads, "one 8-lane row group per head");
@@ -157,9 +224,9 @@ struct DecodeShared {
 // prep: bring in (fused: quantize) the row's query; otherwise sq and sw already hold
 // this row's query from the block's previous item.  `first`: the block's first item (a
 // later item that rewrites sq waits for every wave to be done with it).
-template <bool kFused, bool prep>
+template <bool kFused>
 __device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &sm, int qrow, int64_t blk0,
-                                            bool first) {
+                                            bool prep, bool first) {
     uint8_t *const sq = sm.sq;
     float *const sw = sm.sw;
     uint4 *const snew = sm.snew;
@@ -196,8 +263,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &s
         return;
     }
     const int r = lane & 31, hh = lane >> 5;
-    const int64_t pn = L - 1;                          // fused: the new key's slot
-    const bool has_new = kFused && pn < blk0 + kDecKeysPerBlock;
+    // fused: the new key's slot when this block holds it, else -1 (uniform)
+    const int64_t pn = (kFused && L - 1 < blk0 + kDecKeysPerBlock) ? L - 1 : -1;
 
     if (prep && !first) __syncthreads();               // every wave has its A fragments of the last row
     // Query, weights and (fused) new-key loads, issued before the K loads and never
@@ -247,13 +314,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &s
 #pragma unroll
         for (int c = 0; c < 4; c++) kv[j][c] = src[c];       // rows past L re-read row 0 (masked below)
     };
-    // The fused kernel issues half of the wave's K loads before the query preparation
-    // and half after it: issuing all sixteen first left waves queued behind the
-    // address pipeline for thousands of cycles before their preparation could start,
-    // and the block's barrier waited for the last of them (measured: 14.0 -> 12.2 us).
-    constexpr int kEarlyTiles = kFused ? kDecTiles / 2 : kDecTiles;
+    // Half of the wave's K tiles are issued before the query preparation, the other
+    // half inside the tile pipeline, two steps ahead of their use: issuing all of them
+    // first left waves queued behind the address pipeline before their preparation
+    // could start, and issuing the second half right after it delayed the first MFMAs.
 #pragma unroll
-    for (int j = 0; j < kEarlyTiles; j++) load_tile(j);
+    for (int j = 0; j < kDecFly; j++) load_tile(j);
     // Keep these loads above this point, ahead of the staging and its waits.
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kFused) {
@@ -276,7 +342,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &s
             if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = we;
         }
       }
-        if (has_new && wave == 0) {                    // the new key, spread over wave 0 (2 features a lane)
+        if (pn >= 0 && wave == 0) {                    // the new key, spread over wave 0 (2 features a lane)
             uint32_t kin = kn;
             if (a.rope_cos) rope_row_wave(kin, krc, krs);
             int kj;
@@ -295,8 +361,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &s
         *reinterpret_cast<uint4 *>(sq + (piece >> 3) * kQPitch + 16 * (piece & 7)) = qp0;
         reinterpret_cast<float4 *>(sw)[lane & 15] = wv;    // duplicate stores of equal values
     }
-#pragma unroll
-    for (int j = kEarlyTiles; j < kDecTiles; j++) load_tile(j);
     __syncthreads();
     // A wave whose keys are all masked still runs the tiles (on re-read row 0) and
     // stores -inf: a branch here would let the compiler sink the K loads below the
@@ -312,31 +376,307 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &s
     }
     QueryFrag f;
     convert_query(raw, f);
+    // fused: the lanes of slot pn take the fresh codes and scale (unused when pn < 0)
+    if constexpr (kFused) {
+        const float nscale = sm.snew_scale;
 #pragma unroll
-    for (int p = 0; p < kDecTiles / 2; p++) {
-        if (has_new) {                                 // the lanes holding the new key take the fresh codes
-#pragma unroll
-            for (int h2 = 0; h2 < 2; h2++) {
-                if (key0 + 32 * (2 * p + h2) + r == pn) {
-#pragma unroll
-                    for (int c = 0; c < 4; c++) kv[2 * p + h2][c] = snew[4 * hh + c];
-                }
-            }
-            if (key0 + 64 * p + lane == pn) ks[p] = sm.snew_scale;
-        }
-        const float p0 = score_tile(kv[2 * p], f);
-        const float p1 = score_tile(kv[2 * p + 1], f);
-        // lanes 0-31: tile 2p, key l; lanes 32-63: tile 2p+1, key l-32  ->  key key0 + 64p + l
-        const float sum = halves_sum_pair(p0, p1);
-        const int64_t s = key0 + 64 * p + lane;
-        if (s < T) out[s] = s < L ? sum * ks[p] : -__builtin_inff();
+        for (int p = 0; p < kDecTiles / 2; p++) ks[p] = key0 + 64 * p + lane == pn ? nscale : ks[p];
     }
+    pipelined_tiles<kDecTiles, kDecFly, kFused>(kv, load_tile, f, ks, key0, pn, snew, T, L, out);
 }
 
-template <bool kFused>
-__global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) DecodeShared sm;
-    decode_item<kFused, true>(a, sm, blockIdx.y, (int64_t)blockIdx.x * kDecKeysPerBlock, true);
+// ------------------------------------------------------------------ decode, fused step
+// One block per item, K streamed into LDS by dedicated waves.  A wave that issues
+// loads stalls once the compute unit's memory queue is full (it drains at the chip's
+// HBM rate), so with K loaded into each wave's own registers (decode_item) every wave
+// waits behind its K loads before it can start the query preparation, which the whole
+// item then waits for.  Here four loader waves move the item's 1024 keys (128 KB)
+// into LDS with global_load_lds DMA, in four phases of 32 KB (phase p = tile p of
+// every compute wave), while the eight compute waves issue only their small loads,
+// prepare the query at once, and then take each phase from LDS behind one block
+// barrier per phase (12 waves, 3 per SIMD, so the epilogue reads the folded weights
+// from LDS instead of holding them in registers).
+// LDS layout of a phase: the 8 compute waves' tiles of 32 rows x 128 B, rows in key
+// order; the 16-byte chunk q of a tile's row r sits in slot q ^ ((r >> 1) & 7), so the
+// MFMA B-operand reads (lanes 0-31 rows 0-31, 16 bytes each) touch every bank once per
+// 16 lanes.  A DMA instruction writes 1 KB = 8 consecutive rows, lane i filling slot
+// i % 8 of row i / 8 with the chunk that belongs there.
+constexpr int kDmaComputeWaves = kDecWaves;
+constexpr int kDmaLoaderWaves = 4;
+constexpr int kDmaThreads = 64 * (kDmaComputeWaves + kDmaLoaderWaves);
+constexpr int kDmaPhaseBytes = kDmaComputeWaves * 32 * LK_DIM;            // 32 KB
+constexpr int kDmaPerPhase = kDmaPhaseBytes / 1024 / kDmaLoaderWaves;     // DMA instructions per loader wave
+static_assert(kDmaPerPhase * kDmaLoaderWaves * 1024 == kDmaPhaseBytes, "phase split");
+
+struct DmaShared {
+    uint8_t k[kDecTiles * kDmaPhaseBytes];
+    DecodeShared d;
+};
+
+__device__ __forceinline__ int kslot(int r, int q) { return q ^ ((r >> 1) & 7); }
+
+__global__ void __launch_bounds__(kDmaThreads) decode_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(1024))) DmaShared sm;
+    uint8_t *const sq = sm.d.sq;
+    float *const sw = sm.d.sw;
+    uint4 *const snew = sm.d.snew;
+    const int qrow = blockIdx.y;
+    const int64_t blk0 = (int64_t)blockIdx.x * kDecKeysPerBlock;
+    const int lane = __lane_id(), wave = threadIdx.x >> 6;
+    const int b = qrow / a.rows.S;
+    const int t = qrow - b * a.rows.S;
+    const int64_t T = a.rows.T;
+    const int64_t L = row_len(a.rows, b, t);
+    float *out = a.scores + (int64_t)qrow * T;
+    const bool loader = wave >= kDmaComputeWaves;
+    const int head = threadIdx.x >> 3, sub = threadIdx.x & 7;   // compute waves: this thread's 16 features of a head
+    const bool rope_on = a.rope_cos != nullptr;
+    if (blk0 >= L) {                                   // the whole block is masked: -inf only
+        if (loader) return;
+        for (int64_t s = blk0 + threadIdx.x; s < blk0 + kDecKeysPerBlock && s < T; s += 64 * kDmaComputeWaves)
+            out[s] = -__builtin_inff();
+        if (blk0 == 0 && a.q_fp8_out) {                // a row with L == 0 still returns its quantized query
+            const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
+            const uint4 q0 = qs[0], q1 = qs[1];
+            uint32_t in[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+            if (rope_on) {
+                Rope16 rr;
+                load_rope16(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2), a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), sub, rr);
+                rope_row16(in, rr, sub);
+            }
+            uint32_t codes[4];
+            int j;
+            quantize_row16(in, codes, j);
+            *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) =
+                make_uint4(codes[0], codes[1], codes[2], codes[3]);
+            if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = fold_weight(a.w[(int64_t)qrow * LK_HEADS + head], j);
+        }
+        return;
+    }
+    const uint8_t *kbase = a.k_cache + (int64_t)b * a.cache_seq_stride * LK_DIM;
+    if (loader) {
+        // Loader wave v: in phase p, DMA instruction i covers phase rows 8 (v * kDmaPerPhase + i) .. +7.
+        const int v = wave - kDmaComputeWaves;
+        auto issue_phase = [&](int p) {
+#pragma unroll
+            for (int i = 0; i < kDmaPerPhase; i++) {
+                const int R = 8 * (v * kDmaPerPhase + i) + (lane >> 3);   // row within the phase
+                const int w = R >> 5, r = R & 31;
+                const int q = kslot(r, lane & 7);                         // the chunk this lane's slot holds
+                const int64_t s = blk0 + 32 * (kDecTiles * w + p) + r;
+                const uint8_t *src = kbase + (s < L ? s : 0) * LK_DIM + 16 * q;
+                dma_b128(src, sm.k + p * kDmaPhaseBytes + 1024 * (v * kDmaPerPhase + i));
+            }
+        };
+        // Two phases in flight: issuing all four at once keeps these waves in their
+        // issue loop until half the block has landed, and the first barrier waits
+        // for them (measured slower).
+        issue_phase(0);
+        issue_phase(1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerPhase));
+        __syncthreads();                               // phase 0 landed (and the query is prepared)
+        issue_phase(2);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerPhase));
+        __syncthreads();                               // phase 1
+        issue_phase(3);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerPhase));
+        __syncthreads();                               // phase 2
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();                               // phase 3
+        return;
+    }
+
+    // Compute wave `wave`: keys key0 .. key0 + 127 (its tile p is in phase p).
+    const int64_t key0 = blk0 + (int64_t)wave * kDecKeysPerWave;
+    const int r = lane & 31, hh = lane >> 5;
+    const int64_t pn = L - 1 < blk0 + kDecKeysPerBlock ? L - 1 : -1;   // the new key's slot (uniform)
+    const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
+    const uint4 qp0 = qs[0], qp1 = qs[1];
+    const float wr = a.w[(int64_t)qrow * LK_HEADS + head];
+    const uint32_t kn = reinterpret_cast<const uint32_t *>(a.k_new + (int64_t)b * LK_DIM)[lane];
+    const float *kc_row = rope_on ? a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
+    const float *ks_row = rope_on ? a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
+    const float2 krc = reinterpret_cast<const float2 *>(kc_row)[lane & 15];
+    const float2 krs = reinterpret_cast<const float2 *>(ks_row)[lane & 15];
+    Rope32 rope_row;
+    if (rope_on)
+        load_rope32_uniform(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2),
+                            a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), rope_row);
+    float ks[kDecTiles / 2];
+#pragma unroll
+    for (int p = 0; p < kDecTiles / 2; p++) {
+        const int64_t s = key0 + 64 * p + lane;
+        ks[p] = a.k_scale[(int64_t)b * a.cache_seq_stride + (s < L ? s : 0)];
+    }
+    {
+        uint32_t in[8] = {qp0.x, qp0.y, qp0.z, qp0.w, qp1.x, qp1.y, qp1.z, qp1.w};
+        if (rope_on) {
+            Rope16 rope;
+            pick_rope16(rope_row, sub, rope);
+            rope_row16(in, rope, sub);
+        }
+        uint32_t codes[4];
+        int j;
+        quantize_row16(in, codes, j);
+        const uint4 piece = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+        *reinterpret_cast<uint4 *>(sq + head * kQPitch + 16 * sub) = piece;
+        const float we = fold_weight(wr, j);
+        if (sub == 0) sw[head] = we;
+        if (blk0 == 0 && a.q_fp8_out) {
+            *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) = piece;
+            if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = we;
+        }
+    }
+    if (pn >= 0 && wave == 0) {                        // the new key, spread over wave 0 (2 features a lane)
+        uint32_t kin = kn;
+        if (rope_on) rope_row_wave(kin, krc, krs);
+        int kj;
+        const uint32_t kc = quantize_row_wave(kin, kj);
+        const int64_t row = (int64_t)b * a.cache_seq_stride + pn;
+        reinterpret_cast<uint16_t *>(a.k_cache + row * LK_DIM)[lane] = (uint16_t)kc;
+        reinterpret_cast<uint16_t *>(snew)[lane] = (uint16_t)kc;
+        if (lane == 0) {
+            const float ksc = __builtin_ldexpf(1.0f, kj);
+            a.k_scale[row] = ksc;
+            sm.d.snew_scale = ksc;
+        }
+    }
+    __syncthreads();                                   // query prepared, phase 0 landed
+    QueryRaw raw;
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const uint8_t *qr = sq + (32 * m + r) * kQPitch + 64 * hh;
+#pragma unroll
+        for (int c = 0; c < 4; c++) raw.q[m][c] = *reinterpret_cast<const uint4 *>(qr + 16 * c);
+#pragma unroll
+        for (int g = 0; g < 4; g++) raw.w[m][g] = *reinterpret_cast<const float4 *>(sw + 32 * m + 8 * g + 4 * hh);
+    }
+    QueryFrag f;
+    convert_query(raw, f);
+    // relu_weighted_sum with the weights read from LDS, in the same order.
+    auto relu_weighted_sum_lds = [&](const float16v (&acc2)[2]) {
+        float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 2; m++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const float4 wq = *reinterpret_cast<const float4 *>(sw + 32 * m + 8 * g + 4 * hh);
+                const float wg[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+                    s4[k] = __builtin_fmaf(__builtin_fmaxf(acc2[m][4 * g + k], 0.0f), wg[k], s4[k]);
+            }
+        return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    };
+    {
+        const float nscale = sm.d.snew_scale;
+#pragma unroll
+        for (int p = 0; p < kDecTiles / 2; p++) ks[p] = key0 + 64 * p + lane == pn ? nscale : ks[p];
+    }
+    float16v acc[2][2];
+    float part[2];
+#pragma unroll
+    for (int p = 0; p < kDecTiles; p++) {
+        if (p > 0) __syncthreads();                    // phase p landed
+        uint4 kv[4];
+        const uint8_t *row = sm.k + p * kDmaPhaseBytes + (32 * wave + r) * LK_DIM;
+#pragma unroll
+        for (int c = 0; c < 4; c++) kv[c] = *reinterpret_cast<const uint4 *>(row + 16 * kslot(r, 4 * hh + c));
+        const bool mine = key0 + 32 * p + r == pn;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const uint4 n = snew[4 * hh + c];
+            kv[c].x = mine ? n.x : kv[c].x;
+            kv[c].y = mine ? n.y : kv[c].y;
+            kv[c].z = mine ? n.z : kv[c].z;
+            kv[c].w = mine ? n.w : kv[c].w;
+        }
+        mfma_tile(kv, f, acc[p & 1]);
+        if (p > 0) {
+            part[(p - 1) & 1] = relu_weighted_sum_lds(acc[(p - 1) & 1]);
+            if (p == 2) {
+                const float sum = halves_sum_pair(part[0], part[1]);
+                const int64_t s = key0 + lane;
+                if (s < T) out[s] = s < L ? sum * ks[0] : -__builtin_inff();
+            }
+        }
+    }
+    part[1] = relu_weighted_sum_lds(acc[1]);
+    const float sum = halves_sum_pair(part[0], part[1]);
+    const int64_t s = key0 + 64 + lane;
+    if (s < T) out[s] = s < L ? sum * ks[1] : -__builtin_inff();
+}
+
+// ------------------------------------------------------------------ decode, standalone score
+// lk_index_score with S == 1 and a prepared query: one block per (row, 1024-key block),
+// four waves (one per SIMD), each scoring 256 consecutive keys as 8 tiles through
+// pipelined_tiles with kPipeFly tiles in flight.  Without a preparation to cover, fewer
+// and longer waves stream K best: the query staging is short, and a single wave per
+// SIMD keeps its tiles' loads ahead of its MFMAs.
+constexpr int kPipeWaves = 4;
+constexpr int kPipeThreads = 64 * kPipeWaves;
+constexpr int kPipeTiles = 8;
+constexpr int kPipeFly = 4;
+static_assert(kPipeWaves * kPipeTiles * 32 == kDecKeysPerBlock, "the same key blocks as decode_item");
+static_assert(LK_HEADS * LK_DIM / 16 == 2 * kPipeThreads, "two 16-byte query pieces per thread");
+
+__global__ void __launch_bounds__(kPipeThreads) decode_pipe_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t sq[LK_HEADS * kQPitch];
+    __shared__ __attribute__((aligned(16))) float sw[LK_HEADS];
+    const int qrow = blockIdx.y;
+    const int64_t blk0 = (int64_t)blockIdx.x * kDecKeysPerBlock;
+    const int lane = __lane_id(), wave = threadIdx.x >> 6;
+    const int b = qrow / a.rows.S;
+    const int t = qrow - b * a.rows.S;
+    const int64_t T = a.rows.T;
+    const int64_t L = row_len(a.rows, b, t);
+    const int64_t key0 = blk0 + (int64_t)wave * (32 * kPipeTiles);
+    float *out = a.scores + (int64_t)qrow * T;
+    if (blk0 >= L) {                                   // the whole block is masked: -inf only
+        for (int64_t s = blk0 + threadIdx.x; s < blk0 + kDecKeysPerBlock && s < T; s += kPipeThreads)
+            out[s] = -__builtin_inff();
+        return;
+    }
+    const int r = lane & 31, hh = lane >> 5;
+    // Query pieces tid and tid + 256 (head piece / 8, 16-byte chunk piece % 8) and a
+    // float4 of the weights, issued before the K loads.
+    const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_fp8 + (int64_t)qrow * LK_HEADS * LK_DIM);
+    const uint4 qf0 = qs[threadIdx.x], qf1 = qs[threadIdx.x + kPipeThreads];
+    const float4 wv = reinterpret_cast<const float4 *>(a.w_eff + (int64_t)qrow * LK_HEADS)[lane & 15];
+    float ks[kPipeTiles / 2];
+#pragma unroll
+    for (int p = 0; p < kPipeTiles / 2; p++) {
+        const int64_t s = key0 + 64 * p + lane;
+        ks[p] = a.k_scale[(int64_t)b * a.cache_seq_stride + (s < L ? s : 0)];
+    }
+    const uint8_t *kbase = a.k_cache + (int64_t)b * a.cache_seq_stride * LK_DIM;
+    uint4 kv[kPipeTiles][4];
+    auto load_tile = [&](int j) {
+        const int64_t s = key0 + 32 * j + r;
+        const uint4 *src = reinterpret_cast<const uint4 *>(kbase + (s < L ? s : 0) * LK_DIM + 64 * hh);
+#pragma unroll
+        for (int c = 0; c < 4; c++) kv[j][c] = src[c];       // rows past L re-read row 0 (masked below)
+    };
+#pragma unroll
+    for (int j = 0; j < kPipeFly; j++) load_tile(j);
+    __builtin_amdgcn_sched_barrier(0);
+    const int piece = threadIdx.x;
+    *reinterpret_cast<uint4 *>(sq + (piece >> 3) * kQPitch + 16 * (piece & 7)) = qf0;
+    *reinterpret_cast<uint4 *>(sq + ((piece + kPipeThreads) >> 3) * kQPitch + 16 * (piece & 7)) = qf1;
+    reinterpret_cast<float4 *>(sw)[lane & 15] = wv;    // duplicate stores of equal values
+    __syncthreads();
+    QueryRaw raw;
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const uint8_t *qr = sq + (32 * m + r) * kQPitch + 64 * hh;
+#pragma unroll
+        for (int c = 0; c < 4; c++) raw.q[m][c] = *reinterpret_cast<const uint4 *>(qr + 16 * c);
+#pragma unroll
+        for (int g = 0; g < 4; g++) raw.w[m][g] = *reinterpret_cast<const float4 *>(sw + 32 * m + 8 * g + 4 * hh);
+    }
+    QueryFrag f;
+    convert_query(raw, f);
+    pipelined_tiles<kPipeTiles, kPipeFly, false>(kv, load_tile, f, ks, key0, -1, nullptr, T, L, out);
 }
 
 // Grids of more items than the chip runs at once (many rows, or ragged rows whose key
@@ -397,9 +737,13 @@ __global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeAr
     int prev = -1;
     for (int it = i0; it < i1; it++) {
         while (first_item[row + 1] <= it) row++;
-        const int64_t blk0 = (int64_t)(it - first_item[row]) * kDecKeysPerBlock;
-        if (row != prev) decode_item<kFused, true>(a, sm, row, blk0, it == i0);
-        else decode_item<kFused, false>(a, sm, row, blk0, false);
+        // row and the item's first key are the same in every lane (LDS reads at a
+        // uniform address); saying so keeps the row's addresses, and the RoPE table row
+        // loaded through them, in scalar registers.
+        row = __builtin_amdgcn_readfirstlane(row);
+        const int item0 = __builtin_amdgcn_readfirstlane(first_item[row]);
+        const int64_t blk0 = (int64_t)(it - item0) * kDecKeysPerBlock;
+        decode_item<kFused>(a, sm, row, blk0, row != prev, it == i0);
         prev = row;
     }
 }
@@ -660,7 +1004,8 @@ hipError_t launch_decode_grid(const DecodeArgs &a, hipStream_t stream) {
         return launch(decode_persistent_kernel<kFused>, dim3(grid), dim3(kDecThreads), 0u, stream, a);
     }
     dim3 grid((unsigned)nblk, (unsigned)rows.B);
-    return launch(decode_kernel<kFused>, grid, dim3(kDecThreads), 0u, stream, a);
+    if constexpr (kFused) return launch(decode_kernel, grid, dim3(kDmaThreads), 0u, stream, a);
+    return launch(decode_pipe_kernel, grid, dim3(kPipeThreads), 0u, stream, a);
 }
 
 }  // namespace
