@@ -21,19 +21,20 @@
 // 3. A block scan of the histogram from the top finds that bin b and how many of
 //    its elements are still needed.
 // 4. Inside bin b the exact cut is found: if the bin is taken whole, nothing more;
-//    if it holds at most 64 elements, they are ranked pairwise, NT / 64 lanes per
-//    element (score descending, index ascending); otherwise a radix select walks the
-//    32-bit order-preserving key of the bin's elements with digits of 12, 11 and 9 bits
-//    (10, 10, 10 and 2 with 1024 bins).
+//    if it holds at most NT / 4 elements, they go to LDS and are ranked pairwise
+//    (score descending, index ascending; 4 lanes per element) in step 5; otherwise a
+//    radix select walks the 32-bit order-preserving key of the bin's elements with
+//    digits of 12, 11 and 9 bits (10, 10, 10 and 2 with 1024 bins).
 //    A row whose range is empty or outside [1e-30, 1e30] puts every element in
 //    bin 0 and takes the radix path.
-// 5. The write-out ranks the selected elements with one block-wide scan of packed
+// 5. The write-out places the selected elements with one block-wide scan of packed
 //    per-thread counts, so the result is deterministic: an upper group (the higher
-//    bins and the part of the cut bin above the cut) in increasing index order, then
-//    the cut group (the taken elements at the cut, lowest indices first) in
-//    increasing index order.  Every score of the upper group exceeds every score of
-//    the cut group; the cut group is one value except when a bin or digit is taken
-//    whole.
+//    bins, and after a radix cut the part of the cut bin above the cut) in increasing
+//    index order, then the cut group: after a pairwise cut its `need` best elements in
+//    rank order (score descending, index ascending), each stored by the lanes that
+//    ranked it; otherwise the taken elements at the cut in increasing index order
+//    (lowest indices first).  Every score of the upper group is at least every score
+//    of the cut group (strictly above after a radix cut or a bin taken whole).
 //
 // Wave-level scans and reductions use DPP row shifts and row broadcasts; a reduction
 // over the 16 waves' partial results uses one DPP row.
@@ -45,13 +46,15 @@ namespace {
 // Block shapes: NT threads (1024, or 256 for rows of at most 4096 scores), 16 scores
 // per thread, 4 histogram bins per thread.
 constexpr int kPer = 16;                    // elements per thread
-constexpr int kSmall = 64;                  // a cut bin this small is ranked pairwise
 template <int NT>
 struct Shape {
     static constexpr int kThreads = NT, kWaves = NT / 64, kBins = 4 * NT, kMaxT = NT * kPer;
-    static constexpr int kLanesPerCand = NT / kSmall, kCandsPerLane = kSmall / kLanesPerCand;
+    // A cut bin of at most kSmall elements is ranked pairwise, kLanesPerCand lanes per
+    // candidate (each comparing every kLanesPerCand-th group of 4 candidates).
+    static constexpr int kSmall = NT / 4, kLanesPerCand = NT / kSmall;
     static_assert(kWaves >= 4 && kWaves <= 16 && (kWaves & (kWaves - 1)) == 0, "one DPP row holds the wave totals");
-    static_assert(kCandsPerLane % 4 == 0, "16-byte candidate reads");
+    static_assert(kSmall % 4 == 0 && (kLanesPerCand & (kLanesPerCand - 1)) == 0 && kLanesPerCand <= 4,
+                  "16-byte candidate reads; a candidate's lanes sit in one DPP quad");
 };
 
 // Larger float -> larger key; -0 and +0 map to the same key.
@@ -172,7 +175,7 @@ template <int NT>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8)))
 topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *__restrict__ idx) {
     constexpr int kThreads = Shape<NT>::kThreads, kWaves = Shape<NT>::kWaves, kBins = Shape<NT>::kBins;
-    constexpr int kLanesPerCand = Shape<NT>::kLanesPerCand, kCandsPerLane = Shape<NT>::kCandsPerLane;
+    constexpr int kSmall = Shape<NT>::kSmall, kLanesPerCand = Shape<NT>::kLanesPerCand;
     __shared__ __attribute__((aligned(16))) uint32_t hist_buf[4 + kBins];   // word 3: invalid elements
     uint32_t *const hist = hist_buf + 4;                                     // bins 0 .. kBins-1
     __shared__ __attribute__((aligned(16))) uint32_t wtot[kWaves][4];
@@ -181,7 +184,7 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
     __shared__ uint32_t sel[3];
     __shared__ __attribute__((aligned(16))) uint32_t cand_key[kSmall];
     __shared__ __attribute__((aligned(16))) uint32_t cand_idx[kSmall];
-    __shared__ uint32_t ccount, cut[2];
+    __shared__ uint32_t ccount;
 
     const int row = blockIdx.x;
     const int b = row / rows.S;
@@ -303,61 +306,21 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
         gbits |= (b1 > cb + 1 ? 1u : 0u) << e;
         ebits |= (b1 == cb + 1 ? 1u : 0u) << e;
     }
-    // The cut inside bin cb: of its elements, those whose key & pmask exceeds prefix
-    // join gbits, and the `need` lowest-index ones whose key & pmask equals prefix
-    // stay in ebits.  A bin taken whole needs no cut.
+    // The cut inside bin cb.  A bin taken whole needs none.  A small bin is ranked
+    // pairwise after the write-out barrier (below); its elements leave ebits.  A larger
+    // one is cut by a radix select: of its elements, those whose key & pmask exceeds
+    // prefix join gbits, and the `need` lowest-index ones whose key & pmask equals
+    // prefix stay in ebits.
+    const bool pairwise = need < cnt && cnt <= (uint32_t)kSmall;
     uint32_t prefix = 0, pmask = 0;
-    if (need < cnt && cnt <= kSmall) {
+    if (pairwise) {
         for (uint32_t m = ebits; m; m &= m - 1) {
             const int e = __builtin_ctz(m);
             const uint32_t slot = atomicAdd(&ccount, 1u);
             cand_key[slot] = order_key(v[e]);
             cand_idx[slot] = elem_index<NT>(tid, e);
         }
-        __syncthreads();
-        // Rank of candidate ci = tid / kLanesPerCand among all candidates (score
-        // descending, index ascending): its kLanesPerCand consecutive lanes each compare
-        // it with kCandsPerLane candidates and sum the packed counts (above: low half,
-        // equal with a lower index: high half).
-        {
-            const int ci = tid / kLanesPerCand, q = tid % kLanesPerCand;
-            uint32_t packed = 0, mk = 0, mi = 0;
-            if (ci < (int)cnt) {
-                mk = cand_key[ci];
-                mi = cand_idx[ci];
-#pragma unroll
-                for (int c4 = 0; c4 < kCandsPerLane / 4; c4++) {
-                    const int c0 = kCandsPerLane * q + 4 * c4;
-                    const uint4 kq = *reinterpret_cast<const uint4 *>(cand_key + c0);
-                    const uint4 iq = *reinterpret_cast<const uint4 *>(cand_idx + c0);
-                    const uint32_t kj[4] = {kq.x, kq.y, kq.z, kq.w}, ij[4] = {iq.x, iq.y, iq.z, iq.w};
-#pragma unroll
-                    for (int jj = 0; jj < 4; jj++) {
-                        if (c0 + jj < (int)cnt) {
-                            packed += kj[jj] > mk ? 1u : 0u;
-                            packed += (kj[jj] == mk && ij[jj] < mi) ? 0x10000u : 0u;
-                        }
-                    }
-                }
-            }
-            if constexpr (kLanesPerCand == 16) {
-                packed = row_scan16(packed);               // lane 15 of the DPP row ends with the sum
-            } else {
-#pragma unroll
-                for (int d = 1; d < kLanesPerCand; d <<= 1) packed += (uint32_t)__shfl_xor((int)packed, d, 64);
-            }
-            if (q == kLanesPerCand - 1 && ci < (int)cnt) {
-                const uint32_t gt = packed & 0xFFFFu, eq_before = packed >> 16;
-                if (gt + eq_before == need - 1) {      // the need-th candidate: the cut
-                    cut[0] = mk;
-                    cut[1] = need - gt;
-                }
-            }
-        }
-        __syncthreads();
-        prefix = cut[0];
-        pmask = 0xFFFFFFFFu;
-        need = cut[1];
+        ebits = 0;
     } else if (need < cnt) {
         // Digits of at most log2(kBins) bits from the top: key bits 31-20, 19-9, 8-0 with
         // 4096 bins; 31-22, 21-12, 11-2, 1-0 with 1024.
@@ -381,8 +344,6 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
             pmask |= dm << sh;
             if (need == dcnt) break;                   // the whole digit bin is taken (or the key is exact)
         }
-    }
-    if (pmask) {
         for (uint32_t m = ebits; m; m &= m - 1) {
             const int e = __builtin_ctz(m);
             const uint32_t km = order_key(v[e]) & pmask;
@@ -391,7 +352,9 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
         }
     }
 
-    // 5. Write-out.
+    // 5. Write-out.  The upper group (gbits) takes positions 0 .. n_gt - 1 in index
+    //    order; the cut group takes n_gt .. k - 1: in index order from ebits (a bin taken
+    //    whole, or the radix cut), or, for a pairwise cut, in rank order.
     const uint32_t n_gt = (uint32_t)k - need;
     // Per-row-j counts in 16-bit fields: word 0 = rows 0,1 of gbits; 1 = rows 2,3;
     // words 2, 3 the same for ebits.
@@ -405,7 +368,39 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
 #pragma unroll
     for (int f = 0; f < 4; f++) incl[f] = wave_scan(cnt4[f]);
     if (lane == 63) *reinterpret_cast<uint4 *>(wtot[wave]) = make_uint4(incl[0], incl[1], incl[2], incl[3]);
-    __syncthreads();
+    __syncthreads();                                   // also publishes the pairwise candidates
+    char *const outb = reinterpret_cast<char *>(out);
+    if (pairwise) {
+        // Rank of candidate ci = tid / kLanesPerCand among the cnt candidates (score
+        // descending, index ascending): its lanes each compare it with every
+        // kLanesPerCand-th group of 4 candidates and sum packed counts (above: low half,
+        // equal with a lower index: high half); the last of them stores it at n_gt + rank
+        // when the rank is below `need`.  Ranks are distinct, so each position of the
+        // cut group is written once.
+        const int ci = tid / kLanesPerCand, q = tid % kLanesPerCand;
+        uint32_t packed = 0, mk = 0, mi = 0;
+        if (ci < (int)cnt) {
+            mk = cand_key[ci];
+            mi = cand_idx[ci];
+            for (int g = q; 4 * g < (int)cnt; g += kLanesPerCand) {
+                const uint4 kq = *reinterpret_cast<const uint4 *>(cand_key + 4 * g);
+                const uint4 iq = *reinterpret_cast<const uint4 *>(cand_idx + 4 * g);
+                const uint32_t kj[4] = {kq.x, kq.y, kq.z, kq.w}, ij[4] = {iq.x, iq.y, iq.z, iq.w};
+#pragma unroll
+                for (int jj = 0; jj < 4; jj++) {
+                    if (4 * g + jj < (int)cnt) {
+                        packed += kj[jj] > mk ? 1u : 0u;
+                        packed += (kj[jj] == mk && ij[jj] < mi) ? 0x10000u : 0u;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int d = 1; d < kLanesPerCand; d <<= 1) packed += (uint32_t)__shfl_xor((int)packed, d, 64);
+        const uint32_t rank = (packed & 0xFFFFu) + (packed >> 16);
+        if (q == kLanesPerCand - 1 && ci < (int)cnt && rank < need)
+            *reinterpret_cast<int32_t *>(outb + 4u * (n_gt + rank)) = (int32_t)mi;
+    }
     // The four fields' sums over the lower waves and over all waves: lane l < 16 reads
     // wave l's totals (DPP row 0 holds them all) and the four row scans run together.
     uint32_t before[4], total[4];
@@ -423,7 +418,6 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
     // group holds exactly n_gt elements (every element above the cut, counted by the
     // selection), so its offsets stay below 4 n_gt; the clamp to the row only keeps a
     // store in bounds should that ever fail.
-    char *const outb = reinterpret_cast<char *>(out);
     const uint32_t row_end4 = 4u * (uint32_t)(k - 1);
     uint32_t gbase = 0, ebase = 0;
 #pragma unroll

@@ -67,23 +67,31 @@ def test_topk_ragged_and_causal_rows():
     _check_exact(s2, 2048, g, causal=True, start_pos=2040)
 
 
+def _rank_ordered(r, v):
+    """Scores non-increasing, and indices ascending among equal scores."""
+    dv = np.diff(v)
+    return bool(np.all(dv <= 0) and np.all((dv < 0) | (np.diff(r) > 0)))
+
+
 def test_topk_deterministic_and_ordered():
     rng = np.random.default_rng(7)
-    s = rng.integers(0, 50, (2, 2, 16384)).astype(np.float32)
+    ints = rng.integers(0, 50, (2, 16384)).astype(np.float32)     # ties: the cut bin is one value
+    normal = rng.standard_normal((2, 16384)).astype(np.float32)   # a few distinct values at the cut
+    s = np.stack([ints, normal])                                  # [2 sequences, 2 rows, 16384]
     log("[topk] determinism")
     a = _gpu_topk(s, 2048)
     b = _gpu_topk(s, 2048)
     assert np.array_equal(a, b)
-    # documented order: an upper group in ascending index order, then a cut group in
-    # ascending index order, every score of the upper group above every score of the
-    # cut group
+    # documented order: an upper group in ascending index order, then the cut group,
+    # in ascending index order or (pairwise cut) by score descending, index ascending;
+    # every score of the upper group above every score of the cut group
     for bi in range(2):
         for ti in range(2):
             r = a[bi, ti]
             v = s[bi, ti][r]
             ok = False
             for p in range(len(r) + 1):
-                if np.all(np.diff(r[:p]) > 0) and np.all(np.diff(r[p:]) > 0) and (
+                if np.all(np.diff(r[:p]) > 0) and (np.all(np.diff(r[p:]) > 0) or _rank_ordered(r[p:], v[p:])) and (
                         p == 0 or p == len(r) or v[:p].min() > v[p:].max()):
                     ok = True
                     break
@@ -93,7 +101,8 @@ def test_topk_deterministic_and_ordered():
 @pytest.mark.parametrize("T", [8192, 4096])          # the 1024- and the 256-thread kernel
 def test_topk_cut_paths(T):
     """Rows built so that the bin holding the k-th largest score is taken whole, holds a
-    few elements (ranked pairwise) or many (radix passes), or the row has no spread."""
+    few elements (ranked pairwise: at most 256 with 1024 threads, 64 with 256) or many
+    (radix passes), or the row has no spread."""
     rng = np.random.default_rng(8)
     k = 1000
     rows = []
@@ -114,6 +123,12 @@ def test_topk_cut_paths(T):
     rows.append(wide)
     tiny = (base * 1e-33).astype(np.float32)                   # range below 1e-30
     rows.append(tiny)
+    xk = np.sort(base)[-k]
+    for m in (150, 400):                                       # m distinct values crowd the cut bin:
+        crowded = base.copy()                                  # pairwise (150, 1024 threads) or radix
+        pick = rng.choice(np.flatnonzero(base < xk), m, replace=False)
+        crowded[pick] = (xk + np.arange(1, m + 1) * 2.0**-21 * abs(xk)).astype(np.float32)
+        rows.append(crowded)
     s = np.stack(rows)[:, None, :]
     log(f"[topk] cut paths T={T}")
     for kk in (k, 1, 64, 65, 4096):
