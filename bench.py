@@ -39,7 +39,7 @@ BYTES_PER_QUERY_ROW = 64 * (128 + 4)
 FLOP_PER_PAIR = 2 * 64 * 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 SCORE_SRCS = [os.path.join(ROOT, "sparse_attention_lightning_fp8_amd", "csrc", f)
-              for f in ("score.hip", "quant_device.h", "lk_device.h")]
+              for f in ("score.hip", "quant_device.h", "lk_device.h", "topk_device.h")]
 
 
 def log(msg):
@@ -148,6 +148,25 @@ def raw_calls_fused(wl, s):
     ]
 
 
+def raw_calls_select(wl, s, keep_scores=True):
+    """The same step as raw_calls_fused through one lk_decode_select call (one launch for
+    rows of at most 1024 keys; no score written unless keep_scores)."""
+    import ctypes
+    import torch
+    from sparse_attention_lightning_fp8_amd import _lib
+    lib = _lib.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    cap = s.cache.shape[1]
+    seq_len = s.seq_len.data_ptr() if s.seq_len is not None else None
+    s.rows = _lib.LkRows(wl.B, wl.S, wl.T, wl.start_pos, seq_len, 1 if wl.causal else 0)
+    rows = ctypes.byref(s.rows)
+    return [
+        (lib.lk_decode_select, (s.q.data_ptr(), s.w.data_ptr(), 64, s.k_new.data_ptr(), s.cache.data_ptr(),
+                                s.cache_scale.data_ptr(), cap, rows, s.scores.data_ptr() if keep_scores else None,
+                                None, None, s.q_rope[0], s.q_rope[1], wl.k, s.idx.data_ptr(), stream)),
+    ]
+
+
 def run_step(calls, ev=None, arm=None):
     """One pass of the hot path (lk_prepare: key write + query quantize and weight fold;
     lk_index_score; lk_topk).  `ev` (optional) holds one (start, stop) event pair per
@@ -173,22 +192,29 @@ def make_event_pairs(n_steps, n_kernels):
     return evs
 
 
-def time_workload(api, wl_name, steps, warmup, n_sets, dev, fused=False):
+def time_workload(api, wl_name, steps, warmup, n_sets, dev, fused=False, select=None):
     """Warm up, then time `steps` uninstrumented steps (wall clock between two device
     synchronizations: this gives the step rate), then run the same `steps` again with
     dispatch events armed on every kernel (this gives each kernel's mean duration).
-    `fused` runs the decode step as lk_decode_score + lk_topk."""
+    `fused` runs the decode step as lk_decode_score + lk_topk; `select` ("scores" or
+    "no_scores") as one lk_decode_select call (rows of at most 1024 keys: one launch)."""
     import torch
     from sparse_attention_lightning_fp8_amd import _lib
     from sparse_attention_lightning_fp8_amd import workloads as W
     wl = W.WORKLOADS[wl_name]
     inp = W.make_inputs(wl, seed=0)
     sets = make_sets(api, inp, n_sets, dev)
-    calls = [(raw_calls_fused if fused else raw_calls)(wl, s) for s in sets]
+    if select:
+        calls = [raw_calls_select(wl, s, keep_scores=select == "scores") for s in sets]
+    else:
+        calls = [(raw_calls_fused if fused else raw_calls)(wl, s) for s in sets]
     arm = _lib.load().lk_profile_next_launch
     for i in range(warmup):
         run_step(calls[i % n_sets])
-    names = ["decode_score", "topk"] if fused else ["prepare", "index_score", "topk"]
+    if select:
+        names = ["decode_select"]
+    else:
+        names = ["decode_score", "topk"] if fused else ["prepare", "index_score", "topk"]
     evs = make_event_pairs(steps, len(names))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -554,6 +580,23 @@ def main():
         log(f"ragged_decode_b64: decode_score {rper['decode_score']:.1f} us = {rgbps:.0f} GB/s")
         del rinp
         torch.cuda.empty_cache()
+    # the pages' stated decode step (one sequence at position 1000: 1001 keys, top-256):
+    # two launches (lk_decode_score + lk_topk) against one lk_decode_select launch
+    log("decode_b1_t1001: setting up")
+    torch.cuda.empty_cache()
+    swl, _, s2wall, s2per = time_workload(api, "decode_b1_t1001", args.steps, args.warmup, args.rotate, dev,
+                                          fused=True)
+    _, _, s1wall, s1per = time_workload(api, "decode_b1_t1001", args.steps, args.warmup, args.rotate, dev,
+                                        select="scores")
+    _, _, s0wall, s0per = time_workload(api, "decode_b1_t1001", args.steps, args.warmup, args.rotate, dev,
+                                        select="no_scores")
+    extra["decode_b1_t1001"] = {"two_launch_step_us": s2wall / args.steps * 1e6, "two_launch_kernel_us": s2per,
+                                "select_step_us": s1wall / args.steps * 1e6, "select_kernel_us": s1per,
+                                "select_no_scores_step_us": s0wall / args.steps * 1e6,
+                                "select_no_scores_kernel_us": s0per}
+    log(f"decode_b1_t1001: two launches {s2wall / args.steps * 1e6:.1f} us/step, lk_decode_select "
+        f"{s1wall / args.steps * 1e6:.1f} us/step ({s0wall / args.steps * 1e6:.1f} without scores)")
+    torch.cuda.empty_cache()
     if not args.no_prefill:
         extra.update(time_prefill(api, args.prefill_steps, dev))
 

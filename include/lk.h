@@ -45,6 +45,7 @@ extern "C" {
 #define LK_DIM 128          /* features per index head and per key (page "Index scores") */
 #define LK_HEADS 64         /* index heads (page "Index scores")                       */
 #define LK_TOPK_MAX_T 16384 /* longest score row lk_topk accepts (one row in LDS)      */
+#define LK_SELECT_FUSED_MAX_T 1024 /* rows lk_decode_select scores and selects in one launch */
 #define LK_ROPE_DIM 64      /* leading features RoPE rotates (Indexer.forward excerpt)  */
 #define LK_MLA_HEADS 128    /* attention heads of the MLA decode (page "Join query parts") */
 #define LK_MLA_LATENT 512   /* latent (content) features per head and per cached row    */
@@ -201,6 +202,25 @@ LK_API lk_status lk_decode_score(const uint16_t *q, const float *w, int32_t head
                                  const lk_rows *rows, float *scores, uint8_t *q_fp8_out,
                                  float *w_eff_out, const float *rope_cos, const float *rope_sin,
                                  hipStream_t stream);
+
+/*
+ * The decode step's scores and their per-row top-k from ONE call, as the NKI indexer
+ * returns both (page "DeepSeek-V3.2 Sparse Indexer Kernel API Reference", the call's
+ * returns: scores and top-k indices).  Arguments and results as lk_decode_score, then
+ * idx [B, 1, k] exactly as lk_topk would produce from those scores (same indices in the
+ * same order).  Rows of at most LK_SELECT_FUSED_MAX_T key slots (the pages' stated
+ * decode step, 1001 keys at position 1000, is one) run as ONE kernel launch in which
+ * each block keeps its row's scores in LDS and selects from them there, so the scores
+ * make no round trip through memory; `scores` may then be NULL (not written).  Longer
+ * rows run as lk_decode_score's launch followed by lk_topk's, and need `scores`.
+ * Requires what lk_decode_score and lk_topk require: S == 1, heads == 64,
+ * T <= cache_seq_stride, 1 <= k <= T, T <= LK_TOPK_MAX_T; idx 4-byte aligned.
+ */
+LK_API lk_status lk_decode_select(const uint16_t *q, const float *w, int32_t heads, const uint16_t *k_new,
+                                  uint8_t *k_cache, float *k_scale, int64_t cache_seq_stride,
+                                  const lk_rows *rows, float *scores, uint8_t *q_fp8_out,
+                                  float *w_eff_out, const float *rope_cos, const float *rope_sin,
+                                  int32_t k, int32_t *idx, hipStream_t stream);
 
 /*
  * Per-row top-k of Indexer.forward (index_score.topk), with the NKI indexer's

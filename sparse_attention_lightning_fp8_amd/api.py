@@ -201,6 +201,53 @@ def lk_decode_score(q: torch.Tensor, w: torch.Tensor, k_new: torch.Tensor, k_cac
     return scores
 
 
+def lk_decode_select(q: torch.Tensor, w: torch.Tensor, k_new: torch.Tensor, k_cache: torch.Tensor,
+                     k_scale: torch.Tensor, T: int, k: int, start_pos: int = 0,
+                     seq_len: Optional[torch.Tensor] = None, causal: bool = False,
+                     scores: Optional[torch.Tensor] = None, keep_scores: bool = True,
+                     idx: Optional[torch.Tensor] = None, q_fp8_out: Optional[torch.Tensor] = None,
+                     w_eff_out: Optional[torch.Tensor] = None, rope=None):
+    """lk_decode_score and the per-row top-k from one call: returns (scores [B, 1, T] or
+    None, idx [B, 1, k] int32).  Rows of at most LK_SELECT_FUSED_MAX_T (1024) keys run
+    as one launch; with keep_scores=False (allowed only there) no score is written."""
+    _need(q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[-1] == DIM, "q must be contiguous bf16 [B, H, 128]")
+    H = q.shape[-2]
+    B = q.numel() // (H * DIM) if H > 0 else 0
+    _need(w.dtype == torch.float32 and w.is_contiguous() and w.numel() == B * H, "w must be contiguous float32 [B, H]")
+    _need(k_new.dtype == torch.bfloat16 and k_new.is_contiguous() and k_new.numel() == B * DIM,
+          "k_new must be contiguous bf16 [B, 128]")
+    kc = _byte_view(k_cache)
+    _need(kc.dtype == torch.uint8 and kc.dim() == 3 and kc.shape[2] == DIM and kc.stride(2) == 1
+          and kc.stride(1) == DIM and kc.stride(0) % DIM == 0 and kc.shape[0] >= B, "bad k_cache")
+    ks = k_scale.squeeze(-1) if k_scale.dim() == 3 else k_scale
+    seq_stride = kc.stride(0) // DIM
+    _need(ks.dtype == torch.float32 and ks.dim() == 2 and ks.shape[:2] == kc.shape[:2] and ks.stride(1) == 1
+          and (ks.shape[0] == 1 or ks.stride(0) == seq_stride), "k_scale must share k_cache's sequence stride")
+    _need(0 <= T <= kc.shape[1], "T exceeds the cache capacity")
+    if keep_scores and scores is None:
+        scores = torch.empty((B, 1, T), dtype=torch.float32, device=q.device)
+    if scores is not None:
+        _need(scores.dtype == torch.float32 and scores.numel() == B * T and scores.is_contiguous(), "bad scores")
+    if idx is None:
+        idx = torch.empty((B, 1, k), dtype=torch.int32, device=q.device)
+    _need(idx.dtype == torch.int32 and idx.numel() == B * k and idx.is_contiguous(), "bad idx")
+    q8p = wep = None
+    if q_fp8_out is not None or w_eff_out is not None:
+        _need(q_fp8_out is not None and w_eff_out is not None, "pass both q_fp8_out and w_eff_out, or neither")
+        q8o = _byte_view(q_fp8_out)
+        _need(q8o.dtype == torch.uint8 and q8o.numel() == B * H * DIM and q8o.is_contiguous(), "bad q_fp8_out")
+        _need(w_eff_out.dtype == torch.float32 and w_eff_out.numel() == B * H and w_eff_out.is_contiguous(),
+              "bad w_eff_out")
+        q8p, wep = q8o.data_ptr(), w_eff_out.data_ptr()
+    rows = _rows(B, 1, T, start_pos, seq_len, causal)
+    rc, rs = _rope_args(rope, B, q.device)
+    st = _lib.load().lk_decode_select(q.data_ptr(), w.data_ptr(), H, k_new.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                      seq_stride, ctypes.byref(rows), scores.data_ptr() if scores is not None else None,
+                                      q8p, wep, rc, rs, k, idx.data_ptr(), _stream(q))
+    _lib.check("lk_decode_select", st)
+    return scores, idx
+
+
 def lk_topk(scores: torch.Tensor, k: int, start_pos: int = 0, seq_len: Optional[torch.Tensor] = None,
             causal: bool = False, idx: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Indices [B, S, k] (int32) of the min(k, L) largest scores of each row's valid

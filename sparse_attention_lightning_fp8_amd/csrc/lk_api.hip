@@ -15,6 +15,10 @@ hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t
                                float *k_scale, int64_t cache_seq_stride, const RowsDev &rows, float *scores,
                                uint8_t *q_fp8_out, float *w_eff_out, const float *rope_cos,
                                const float *rope_sin, hipStream_t stream);
+hipError_t launch_decode_select(const uint16_t *q, const float *w, const uint16_t *k_new, uint8_t *k_cache,
+                                float *k_scale, int64_t cache_seq_stride, const RowsDev &rows, float *scores,
+                                uint8_t *q_fp8_out, float *w_eff_out, const float *rope_cos,
+                                const float *rope_sin, int32_t k, int32_t *idx, hipStream_t stream);
 hipError_t launch_probe_empty(int32_t blocks, hipStream_t stream);
 hipError_t launch_probe_read(const void *src, uint64_t bytes, uint32_t *sink, int32_t blocks, hipStream_t stream);
 hipError_t launch_probe_fp8_score(const uint8_t *q_fp8, const float *w_eff, const uint8_t *k_cache,
@@ -215,6 +219,34 @@ LK_API lk_status lk_decode_score(const uint16_t *q, const float *w, int32_t head
     if (rows->B > kMaxGridYZ || rows->T > kMaxGridX) return LK_E_UNSUPPORTED;
     return from_hip(lk::launch_decode_score(q, w, k_new, k_cache, k_scale, cache_seq_stride, to_dev(*rows), scores,
                                             q_fp8_out, w_eff_out, rope_cos, rope_sin, stream));
+}
+
+LK_API lk_status lk_decode_select(const uint16_t *q, const float *w, int32_t heads, const uint16_t *k_new,
+                                  uint8_t *k_cache, float *k_scale, int64_t cache_seq_stride,
+                                  const lk_rows *rows, float *scores, uint8_t *q_fp8_out, float *w_eff_out,
+                                  const float *rope_cos, const float *rope_sin, int32_t k, int32_t *idx,
+                                  hipStream_t stream) {
+    DisarmOnExit disarm;
+    lk_status st = check_rows(rows);
+    if (st != LK_OK) return st;
+    st = check_rope(rope_cos, rope_sin);
+    if (st != LK_OK) return st;
+    if (cache_seq_stride < 0 || rows->T > cache_seq_stride) return LK_E_SHAPE;
+    if (rows->S > 1) return LK_E_SHAPE;
+    if (k < 1 || k > rows->T) return LK_E_SHAPE;
+    if (heads != LK_HEADS) return LK_E_UNSUPPORTED;
+    if (rows->T > LK_TOPK_MAX_T) return LK_E_UNSUPPORTED;
+    if ((q_fp8_out == nullptr) != (w_eff_out == nullptr)) return LK_E_NULL;
+    if (rows->B == 0 || rows->S == 0) return LK_OK;
+    if (!q || !w || !k_new || !k_cache || !k_scale || !idx) return LK_E_NULL;
+    if (!scores && rows->T > LK_SELECT_FUSED_MAX_T) return LK_E_NULL;
+    if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(k_cache, 16) || !aligned(q_fp8_out, 16) ||
+        !aligned(w, 4) || !aligned(w_eff_out, 4) || !aligned(k_scale, 4) || !aligned(scores, 4) ||
+        !aligned(idx, 4) || !aligned(rows->seq_len, 4))
+        return LK_E_UNSUPPORTED;
+    if (rows->B > kMaxGridYZ || rows->T > kMaxGridX) return LK_E_UNSUPPORTED;
+    return from_hip(lk::launch_decode_select(q, w, k_new, k_cache, k_scale, cache_seq_stride, to_dev(*rows), scores,
+                                             q_fp8_out, w_eff_out, rope_cos, rope_sin, k, idx, stream));
 }
 
 LK_API lk_status lk_topk(const float *scores, const lk_rows *rows, int32_t k, int32_t *idx, hipStream_t stream) {

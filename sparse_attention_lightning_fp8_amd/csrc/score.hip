@@ -18,8 +18,11 @@
 // (heads 32m..32m+31) holds, in lane l, key (l % 32) and heads
 // 32m + 8(i/4) + 4(l/32) + (i%4) for i < 16, so a lane sums 32 heads in registers and
 // one cross-half swap (v_permlane32_swap) completes the 64-head sum.
+#include <type_traits>
+
 #include "lk_device.h"
 #include "quant_device.h"
+#include "topk_device.h"
 
 namespace lk {
 namespace {
@@ -166,7 +169,9 @@ __device__ __forceinline__ void pipelined_tiles(uint4 (&kv)[kTiles][4], LoadTile
 // Work is cut into items of kDecKeysPerBlock (1024) consecutive keys of one query row.
 // Three kernels cover them:
 //  - decode_kernel (the fused step, one block per item): loader waves stream the
-//    item's keys into LDS while compute waves prepare the query;
+//    item's keys into LDS while compute waves prepare the query; as
+//    decode_kernel<true> (lk_decode_select, rows of one item) the block also keeps
+//    its scores in LDS and its loader waves then select the row's top-k from there;
 //  - decode_pipe_kernel (lk_index_score with a prepared query, one block per item):
 //    four waves with K in registers;
 //  - decode_persistent_kernel (both, when the items outnumber what the chip runs at
@@ -210,7 +215,9 @@ struct DecodeArgs {
     float *k_scale;             // [B, stride]
     int64_t cache_seq_stride;
     RowsDev rows;
-    float *scores;              // [B, T]
+    float *scores;              // [B, T]; may be NULL in the fused select kernel
+    int32_t k;                  // fused select: the top-k of each row into idx [B, k]
+    int32_t *idx;
 };
 
 struct DecodeShared {
@@ -413,10 +420,20 @@ struct DmaShared {
     DecodeShared d;
 };
 
+// Fused select (rows of at most one key block): the block's scores, then the row's
+// top-k run by the loader waves once the compute waves are done.
+struct SelectShared {
+    float sc[kDecKeysPerBlock] __attribute__((aligned(16)));
+    TopkShared<64 * kDmaLoaderWaves> t;
+};
+static_assert(64 * kDmaLoaderWaves == 256 && Shape<256>::kMaxT >= kDecKeysPerBlock, "the loader waves' top-k shape");
+
 __device__ __forceinline__ int kslot(int r, int q) { return q ^ ((r >> 1) & 7); }
 
+template <bool kSelect>
 __global__ void __launch_bounds__(kDmaThreads) decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) DmaShared sm;
+    __shared__ std::conditional_t<kSelect, SelectShared, char> ssel;
     uint8_t *const sq = sm.d.sq;
     float *const sw = sm.d.sw;
     uint4 *const snew = sm.d.snew;
@@ -427,14 +444,19 @@ __global__ void __launch_bounds__(kDmaThreads) decode_kernel(DecodeArgs a) {
     const int t = qrow - b * a.rows.S;
     const int64_t T = a.rows.T;
     const int64_t L = row_len(a.rows, b, t);
-    float *out = a.scores + (int64_t)qrow * T;
+    float *out = a.scores ? a.scores + (int64_t)qrow * T : nullptr;   // NULL only in the fused select
     const bool loader = wave >= kDmaComputeWaves;
     const int head = threadIdx.x >> 3, sub = threadIdx.x & 7;   // compute waves: this thread's 16 features of a head
     const bool rope_on = a.rope_cos != nullptr;
+    // The fused select may leave the scores out; the select kernel has one block per row.
+    const bool keep_scores = !kSelect || a.scores != nullptr;
     if (blk0 >= L) {                                   // the whole block is masked: -inf only
         if (loader) return;
-        for (int64_t s = blk0 + threadIdx.x; s < blk0 + kDecKeysPerBlock && s < T; s += 64 * kDmaComputeWaves)
-            out[s] = -__builtin_inff();
+        if (keep_scores)
+            for (int64_t s = blk0 + threadIdx.x; s < blk0 + kDecKeysPerBlock && s < T; s += 64 * kDmaComputeWaves)
+                out[s] = -__builtin_inff();
+        if constexpr (kSelect)                         // L == 0: nothing is selected
+            for (int j = threadIdx.x; j < a.k; j += 64 * kDmaComputeWaves) a.idx[(int64_t)qrow * a.k + j] = -1;
         if (blk0 == 0 && a.q_fp8_out) {                // a row with L == 0 still returns its quantized query
             const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
             const uint4 q0 = qs[0], q1 = qs[1];
@@ -483,6 +505,11 @@ __global__ void __launch_bounds__(kDmaThreads) decode_kernel(DecodeArgs a) {
         __syncthreads();                               // phase 2
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();                               // phase 3
+        if constexpr (kSelect) {
+            __syncthreads();                           // the block's scores are in LDS
+            topk_row<64 * kDmaLoaderWaves>(ssel.sc, kDecKeysPerBlock, L, a.k, a.idx + (int64_t)qrow * a.k,
+                                           (int)threadIdx.x - 64 * kDmaComputeWaves, ssel.t.view());
+        }
         return;
     }
 
@@ -597,14 +624,21 @@ __global__ void __launch_bounds__(kDmaThreads) decode_kernel(DecodeArgs a) {
             if (p == 2) {
                 const float sum = halves_sum_pair(part[0], part[1]);
                 const int64_t s = key0 + lane;
-                if (s < T) out[s] = s < L ? sum * ks[0] : -__builtin_inff();
+                const float v = s < L ? sum * ks[0] : -__builtin_inff();
+                if (s < T && keep_scores) out[s] = v;
+                if constexpr (kSelect) ssel.sc[s - blk0] = v;
             }
         }
     }
     part[1] = relu_weighted_sum_lds(acc[1]);
     const float sum = halves_sum_pair(part[0], part[1]);
     const int64_t s = key0 + 64 + lane;
-    if (s < T) out[s] = s < L ? sum * ks[1] : -__builtin_inff();
+    const float v = s < L ? sum * ks[1] : -__builtin_inff();
+    if (s < T && keep_scores) out[s] = v;
+    if constexpr (kSelect) {
+        ssel.sc[s - blk0] = v;
+        __syncthreads();                               // hand the scores to the loader waves' top-k
+    }
 }
 
 // ------------------------------------------------------------------ decode, standalone score
@@ -1004,7 +1038,7 @@ hipError_t launch_decode_grid(const DecodeArgs &a, hipStream_t stream) {
         return launch(decode_persistent_kernel<kFused>, dim3(grid), dim3(kDecThreads), 0u, stream, a);
     }
     dim3 grid((unsigned)nblk, (unsigned)rows.B);
-    if constexpr (kFused) return launch(decode_kernel, grid, dim3(kDmaThreads), 0u, stream, a);
+    if constexpr (kFused) return launch(decode_kernel<false>, grid, dim3(kDmaThreads), 0u, stream, a);
     return launch(decode_pipe_kernel, grid, dim3(kPipeThreads), 0u, stream, a);
 }
 
@@ -1061,6 +1095,38 @@ hipError_t launch_decode_score(const uint16_t *q, const float *w, const uint16_t
     a.rows = rows;
     a.scores = scores;
     return launch_decode_grid<true>(a, stream);
+}
+
+hipError_t launch_topk(const float *scores, const RowsDev &rows, int32_t k, int32_t *idx, hipStream_t stream);
+
+// The fused decode step with its top-k: rows of at most one key block in one launch
+// (decode_kernel<true>: scores kept in LDS, the top-k by the block's loader waves);
+// longer rows as the fused score launch followed by the top-k launch (scores required).
+hipError_t launch_decode_select(const uint16_t *q, const float *w, const uint16_t *k_new, uint8_t *k_cache,
+                                float *k_scale, int64_t cache_seq_stride, const RowsDev &rows, float *scores,
+                                uint8_t *q_fp8_out, float *w_eff_out, const float *rope_cos,
+                                const float *rope_sin, int32_t k, int32_t *idx, hipStream_t stream) {
+    if (rows.T > kDecKeysPerBlock) {
+        const hipError_t e = launch_decode_score(q, w, k_new, k_cache, k_scale, cache_seq_stride, rows, scores,
+                                                 q_fp8_out, w_eff_out, rope_cos, rope_sin, stream);
+        return e != hipSuccess ? e : launch_topk(scores, rows, k, idx, stream);
+    }
+    DecodeArgs a{};
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
+    a.q_bf16 = q;
+    a.w = w;
+    a.k_new = k_new;
+    a.q_fp8_out = q_fp8_out;
+    a.w_eff_out = w_eff_out;
+    a.k_cache = k_cache;
+    a.k_scale = k_scale;
+    a.cache_seq_stride = cache_seq_stride;
+    a.rows = rows;
+    a.scores = scores;
+    a.k = k;
+    a.idx = idx;
+    return launch(decode_kernel<true>, dim3(1, (unsigned)rows.B), dim3(kDmaThreads), 0u, stream, a);
 }
 
 }  // namespace lk

@@ -156,12 +156,14 @@ def gpu_pipeline(inp: W.Inputs, device="cuda:0", rope: bool = False) -> GpuResul
     return GpuResult(cache, cache_scale, q_fp8, w_eff, q_scale, scores, idx)
 
 
-def gpu_pipeline_fused(inp: W.Inputs, device="cuda:0", rope: bool = False) -> GpuResult:
+def gpu_pipeline_fused(inp: W.Inputs, device="cuda:0", rope: bool = False, select: bool = False,
+                       keep_scores: bool = True) -> GpuResult:
     """The fused decode step through the C ABI: the cache prefix [0, L-1) of each
     sequence is written first (slot L-1 and beyond hold 0xAA garbage), then one
     lk_decode_score launch writes the new key at L-1, quantizes the query and scores,
-    then lk_topk.  With `rope`, the prefix keys are rotated at their positions and the
-    step's query and new key at position L-1."""
+    then lk_topk.  With `select`, the same step as one lk_decode_select call (scores
+    left out when not `keep_scores`).  With `rope`, the prefix keys are rotated at their
+    positions and the step's query and new key at position L-1."""
     from sparse_attention_lightning_fp8_amd import api
     wl = inp.wl
     assert wl.S == 1
@@ -184,9 +186,15 @@ def gpu_pipeline_fused(inp: W.Inputs, device="cuda:0", rope: bool = False) -> Gp
     w = inp.w.to(device).reshape(wl.B, 64)
     q_fp8 = torch.empty((wl.B, 1, 64, 128), dtype=torch.uint8, device=device)
     w_eff = torch.empty((wl.B, 1, 64), dtype=torch.float32, device=device)
-    scores = api.lk_decode_score(q, w, new_rows, cache, cache_scale, wl.T, start_pos=wl.start_pos,
-                                 seq_len=seq_len, causal=wl.causal, q_fp8_out=q_fp8, w_eff_out=w_eff, rope=rope_t)
-    idx = api.lk_topk(scores, wl.k, start_pos=wl.start_pos, seq_len=seq_len, causal=wl.causal)
+    if select:
+        scores, idx = api.lk_decode_select(q, w, new_rows, cache, cache_scale, wl.T, wl.k, start_pos=wl.start_pos,
+                                           seq_len=seq_len, causal=wl.causal, keep_scores=keep_scores,
+                                           q_fp8_out=q_fp8, w_eff_out=w_eff, rope=rope_t)
+    else:
+        scores = api.lk_decode_score(q, w, new_rows, cache, cache_scale, wl.T, start_pos=wl.start_pos,
+                                     seq_len=seq_len, causal=wl.causal, q_fp8_out=q_fp8, w_eff_out=w_eff,
+                                     rope=rope_t)
+        idx = api.lk_topk(scores, wl.k, start_pos=wl.start_pos, seq_len=seq_len, causal=wl.causal)
     torch.cuda.synchronize()
     return GpuResult(cache, cache_scale, q_fp8, w_eff, None, scores, idx)
 

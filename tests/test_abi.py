@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     assert syms == sorted(["lk_quantize_keys", "lk_quantize_queries", "lk_index_score", "lk_topk",
-                           "lk_prepare", "lk_decode_score", "lk_sparse_mla_workspace_size",
+                           "lk_prepare", "lk_decode_score", "lk_decode_select", "lk_sparse_mla_workspace_size",
                            "lk_sparse_mla_decode", "lk_sparse_mla_decode_static", "lk_profile_next_launch",
                            "lk_probe_empty", "lk_probe_read", "lk_probe_fp8_mfma_score", "lk_status_string",
                            "lk_abi_version"])
@@ -140,6 +140,32 @@ def test_decode_score_validation(lib):
     assert f(A, A, 64, A, A, A, 16, rows(), A, None, None, A, None, None) == E_NULL     # RoPE pair
     assert f(A, A, 64, A, A, A, 16, rows(), A, None, None, A + 8, A, None) == E_UNSUP
     assert f(None, None, 64, None, None, None, 16, rows(B=0), None, None, None, None, None, None) == OK
+
+
+def test_decode_select_validation(lib):
+    f = lib.lk_decode_select
+    #   q  w   H   kn k_cache k_scale stride rows  scores q8o  weo  cos  sin  k  idx stream
+    def c(q=A, w=A, H=64, kn=A, kc=A, ks=A, stride=16, r=None, sc=A, q8o=None, weo=None, cos=None, sin=None,
+          k=8, idx=A):
+        return f(q, w, H, kn, kc, ks, stride, rows() if r is None else r, sc, q8o, weo, cos, sin, k, idx, None)
+    assert f(A, A, 64, A, A, A, 16, None, A, None, None, None, None, 8, A, None) == E_NULL
+    assert c(r=rows(S=2)) == E_SHAPE                                         # decode rows only
+    assert c(r=rows(T=17)) == E_SHAPE                                        # T beyond the cache
+    assert c(k=0) == E_SHAPE
+    assert c(k=17) == E_SHAPE                                                # k beyond the row
+    assert c(H=32) == E_UNSUP
+    assert c(r=rows(T=16385), stride=16385) == E_UNSUP                       # beyond one top-k row
+    assert c(q8o=A) == E_NULL                                                # one optional output
+    assert c(q=None) == E_NULL
+    assert c(idx=None) == E_NULL
+    assert c(cos=A) == E_NULL                                                # RoPE tables come in pairs
+    # scores may be left out only where the whole step is one launch (T <= 1024)
+    assert c(sc=None, r=rows(T=1025), stride=1025, idx=A + 2) == E_NULL
+    assert c(sc=None, idx=A + 2) == E_UNSUP                                  # passes the NULL check, misaligned idx
+    assert c(q=A + 8) == E_UNSUP
+    assert c(sc=A + 2) == E_UNSUP
+    assert c(r=rows(B=70000, T=16)) == E_UNSUP                               # grid limit
+    assert c(q=None, w=None, kn=None, kc=None, ks=None, sc=None, idx=None, r=rows(B=0)) == OK
 
 
 def test_topk_validation(lib):
