@@ -629,7 +629,7 @@ def main():
                    "topk": wl.k, "rotated_input_copies": args.rotate},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
-                     "kernel": "decode_kernel (lk_decode_score)", "algorithmic_bytes": score_bytes},
+                     "kernel": "decode_kernel<false> (lk_decode_score)", "algorithmic_bytes": score_bytes},
         "cpu_baseline": cpu,
         "extra": extra,
     }
