@@ -109,3 +109,17 @@ def test_first_row_past_one_block():
     sel = gpu_pipeline_fused(inp, select=True)
     _assert_same(two, sel, inp.wl)
     _check_oracle(inp, sel, list(range(inp.wl.B)))
+
+
+def test_causal_rows():
+    """Decode rows with the causal limit inside the row (L = start_pos + 1 < T): the slots
+    past it are -inf and out of the selection, in one launch and past one block."""
+    for T, k in ((1001, 256), (3000, 700)):
+        wl = W.Workload(name=f"select_causal_t{T}", B=3, S=1, T=T, cap=T, start_pos=T // 2, k=k,
+                        causal=True, ragged=False)
+        inp = W.make_inputs(wl, seed=14)
+        log(f"[select] causal rows, T={T}, start_pos={wl.start_pos}, k={k}")
+        two = gpu_pipeline_fused(inp)
+        sel = gpu_pipeline_fused(inp, select=True)
+        _assert_same(two, sel, wl)
+        _check_oracle(inp, sel, list(range(wl.B)))
