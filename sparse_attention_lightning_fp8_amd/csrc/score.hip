@@ -784,14 +784,15 @@ __global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeAr
 
 // ------------------------------------------------------------------ prefill (S > 1)
 // A block of 8 waves (two per SIMD) owns 8 consecutive query tokens of one sequence (one
-// per wave) and a slice of up to 4096 keys, taken as chunks of 128.  Each chunk is read
-// from HBM once per block, converted to f16 once and kept in LDS, where every wave
-// streams it through the MFMA against its own query held in registers; the chunks are
-// double buffered, so one barrier per chunk publishes the next one.
-//  - Staging layout: thread (wave w, lane l) stages key row 32 (w % 4) + l % 32 of the
-//    chunk, quarter (l / 32) + 2 (w / 4) of the row, and writes it to LDS in the MFMA
-//    B-operand read pattern (rows in lanes 0-31, the next piece of the row in lanes
-//    32-63): the pattern in which the 16-byte LDS accesses are free of bank conflicts.
+// per wave) and a slice of up to 4096 keys, taken as chunks of 256.  Each chunk is read
+// from HBM once per block, converted to f16 once and kept in LDS (two 68 KB buffers),
+// where every wave streams it through the MFMA against its own query held in registers;
+// the chunks are double buffered, so one barrier per chunk (eight tiles per wave)
+// publishes the next one.
+//  - Staging layout: thread (wave w, lane l) stages key row 32 w + l % 32 of the chunk,
+//    half l / 32 of the row, and writes it to LDS in the MFMA B-operand read pattern
+//    (rows in lanes 0-31, the other half of the row in lanes 32-63): the pattern in
+//    which the 16-byte LDS accesses are free of bank conflicts.
 //  - The next chunk's loads are issued at the start of a chunk; their conversion and LDS
 //    writes ride in the MFMA stream of the chunk's third tile.
 //  - Chunks valid for the wave's row run as one software pipeline across chunk
@@ -805,9 +806,9 @@ __global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeAr
 //    gives every XCD every slice equally often instead of pinning slice x to XCD x.
 constexpr int kPreWaves = 8;                          // query tokens per block, one per wave
 constexpr int kPreThreads = 64 * kPreWaves;
-constexpr int kPreChunk = 128;                        // keys per LDS buffer
+constexpr int kPreChunk = 256;                        // keys per LDS buffer
 constexpr int kPreTiles = kPreChunk / 32;
-constexpr int kPreChunks = 32;                        // chunks per slice
+constexpr int kPreChunks = 16;                        // chunks per slice
 constexpr int kPreSlice = kPreChunk * kPreChunks;     // keys per work item
 constexpr int kPreRowBytes = 2 * LK_DIM + 16;         // f16 row + 16 B pad against bank conflicts
 constexpr int kPreRowGroups = kPreChunk / 32;         // 32-row groups of a chunk

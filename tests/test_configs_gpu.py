@@ -15,8 +15,9 @@ from tests._parity import OracleCase, compare_scores, compare_topk, gpu_pipeline
 pytestmark = pytest.mark.gpu
 
 # (workload, rows to check as (b, t)).  Prefill rows cover every position of an 8-token
-# block (the prefill kernel's token group), both sides of 128-key chunk and 2048/4096-key
-# slice edges, rows whose causal diagonal ends mid-chunk, and a spread over token groups.
+# block (the prefill kernel's token group), both sides of 256-key chunk edges (and of
+# 128-key half-chunk edges), of 2048/4096-key slice edges, rows whose causal diagonal ends
+# mid-chunk, and a spread over token groups.
 def _prefill_rows(S, seqs, extra, group_step):
     ts = set(range(8)) | set(range(S - 8, S)) | set(extra)
     ts |= {8 * g + g % 8 for g in range(0, S // 8, group_step)}
@@ -28,11 +29,13 @@ SAMPLES = {
     "decode_b16_t16384": [(b, 0) for b in range(16)],
     "ragged_decode_b64": "ragged",
     # causal 4096 x 4096: row t has t + 1 keys
-    "prefill_s4096": _prefill_rows(4096, [0], [126, 127, 128, 129, 255, 256, 1000, 2046, 2047, 2048, 2049,
-                                                3001, 4094], 11),
+    "prefill_s4096": _prefill_rows(4096, [0], [126, 127, 128, 129, 255, 256, 511, 512, 1000, 2046, 2047,
+                                                2048, 2049, 3001, 4094], 11),
     # 4096 new tokens at 12288..16383: row t has 12289 + t keys; slice edges at keys
-    # 4096, 8192, 12288; chunk-aligned lengths at t = 127, 2047, 3967
-    "chunked_prefill_b2_s4096": _prefill_rows(4096, [0, 1], [126, 127, 128, 1023, 2046, 2047, 2048, 3967], 23),
+    # 4096, 8192, 12288; 256-key aligned lengths at t = 255, 2047, 3839, 128-key aligned
+    # at t = 127, 3967
+    "chunked_prefill_b2_s4096": _prefill_rows(4096, [0, 1], [126, 127, 128, 254, 255, 256, 1023, 2046, 2047,
+                                                              2048, 3839, 3840, 3967], 23),
 }
 
 
