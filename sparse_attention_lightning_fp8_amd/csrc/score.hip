@@ -581,18 +581,27 @@ __global__ void __launch_bounds__(kDmaThreads) decode_kernel(DecodeArgs a) {
     QueryFrag f;
     convert_query(raw, f);
     // relu_weighted_sum with the weights read from LDS, in the same order.
+    // The weight quads are read two at a time: one at a time, the register budget made
+    // the compiler wait out each LDS read before the next (eight round trips per tile).
     auto relu_weighted_sum_lds = [&](const float16v (&acc2)[2]) {
         float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int m = 0; m < 2; m++)
+        for (int i0 = 0; i0 < 8; i0 += 2) {
+            float4 wq[2];
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const float4 wq = *reinterpret_cast<const float4 *>(sw + 32 * m + 8 * g + 4 * hh);
-                const float wg[4] = {wq.x, wq.y, wq.z, wq.w};
+            for (int i = 0; i < 2; i++) {
+                const int m = (i0 + i) >> 2, g = (i0 + i) & 3;
+                wq[i] = *reinterpret_cast<const float4 *>(sw + 32 * m + 8 * g + 4 * hh);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int m = (i0 + i) >> 2, g = (i0 + i) & 3;
+                const float wg[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
 #pragma unroll
                 for (int k = 0; k < 4; k++)
                     s4[k] = __builtin_fmaf(__builtin_fmaxf(acc2[m][4 * g + k], 0.0f), wg[k], s4[k]);
             }
+        }
         return (s4[0] + s4[1]) + (s4[2] + s4[3]);
     };
     {
