@@ -167,15 +167,18 @@ __device__ __forceinline__ void pipelined_tiles(uint4 (&kv)[kTiles][4], LoadTile
 
 // ------------------------------------------------------------------ decode (S == 1)
 // Work is cut into items of kDecKeysPerBlock (1024) consecutive keys of one query row.
-// Three kernels cover them:
+// Four kernels cover them:
 //  - decode_kernel (the fused step, one block per item): loader waves stream the
 //    item's keys into LDS while compute waves prepare the query; as
 //    decode_kernel<true> (lk_decode_select, rows of one item) the block also keeps
 //    its scores in LDS and its loader waves then select the row's top-k from there;
+//  - decode_units_kernel (the fused step when the items outnumber what the chip runs
+//    at once): the same loader-wave block over a balanced run of 512-key units of one
+//    row, one per compute unit;
 //  - decode_pipe_kernel (lk_index_score with a prepared query, one block per item):
 //    four waves with K in registers;
-//  - decode_persistent_kernel (both, when the items outnumber what the chip runs at
-//    once): one block per compute unit walks a range of items with decode_item.
+//  - decode_persistent_kernel (lk_index_score when the items outnumber what the chip
+//    runs at once): one block per compute unit walks a range of items with decode_item.
 // In decode_item, one wave scores 128 consecutive keys (4 tiles of 32) and a block of
 // kDecWaves waves covers the item.  Each lane loads its 4 x 64 bytes of K straight
 // into the B-operand registers (keys are read exactly once, so staging K in LDS brings
@@ -650,6 +653,345 @@ __global__ void __launch_bounds__(kDmaThreads) decode_kernel(DecodeArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ decode, fused, many items
+// The fused step when the rows' 1024-key items outnumber what one wave of blocks covers
+// (ragged rows among them): one loader-wave block per compute unit, each scoring a run
+// of consecutive 512-key units of one row, so one query preparation serves the whole
+// run.  A unit is two 32-key tiles of every compute wave (wave w takes keys 64 w .. 64 w
+// + 63 of the unit); the loaders stream its two phases through the same four 32 KB
+// buffers, two phases ahead, and every phase ends in one block barrier as in
+// decode_kernel.  Runs never cross a row and are balanced at unit granularity: every
+// block derives the same schedule from the row lengths (row r has
+// u_r = max(1, ceil(L_r / 512)) units; the cap c is the smallest for which the rows'
+// ceil(u_r / c) runs fit the grid; row r's units are split into that many runs of equal
+// size up to one), and block g takes run g.  A row with L_r = 0 gets one empty run that
+// sweeps it to -inf (and writes its quantized query when that is requested); the last
+// run of every row sweeps the slots past its units.
+constexpr int kUnitKeys = kDecKeysPerBlock / 2;                 // 512
+constexpr int kUnitTiles = kUnitKeys / (32 * kDmaComputeWaves); // 2 tiles per compute wave
+constexpr int kUnitMaxRows = kDecThreads;                         // rows the schedule takes (one per thread)
+static_assert(kUnitTiles == 2 && kDecTiles == 4, "a unit is two phases of the four-buffer ring");
+static_assert(kUnitMaxRows <= kDmaThreads, "one row per thread in the schedule");
+
+struct UnitShared {
+    DmaShared s;
+    int64_t run_len;                                   // the row's valid length L
+    int32_t run[5];                                    // this block's row, first unit, units, last, runs in all
+    int32_t part[kDmaThreads / 64];                    // per-wave partial sums of the schedule
+};
+
+__global__ void __launch_bounds__(kDmaThreads) decode_units_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(1024))) UnitShared us;
+    DmaShared &sm = us.s;
+    uint8_t *const sq = sm.d.sq;
+    float *const sw = sm.d.sw;
+    uint4 *const snew = sm.d.snew;
+    const int nrows = a.rows.B;                        // S == 1; nrows <= kUnitMaxRows (host check)
+    const int tid = threadIdx.x, lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // ---- the schedule (every block the same).  Up to 64 rows, wave 0 derives it with
+    // lane shuffles and hands this block's run to the others through LDS (one barrier);
+    // more rows take the block-wide form (one row per thread, block sums and a scan).
+    const int G = gridDim.x, g = blockIdx.x;
+    if (nrows <= 64) {
+        if (wave == 0) {
+            int64_t Lr = 0;
+            int u = 0;
+            if (lane < nrows) {
+                Lr = row_len(a.rows, lane, 0);
+                const int64_t ur = (Lr + kUnitKeys - 1) / kUnitKeys;
+                u = ur < 1 ? 1 : (int)ur;
+            }
+            auto wave_sum = [&](int x) {
+#pragma unroll
+                for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+                return x;
+            };
+            int cap = (wave_sum(u) + G - 1) / G;
+            for (;; cap++)                             // ends by cap = max u_r (then nrows <= G runs)
+                if (wave_sum(lane < nrows ? (u + cap - 1) / cap : 0) <= G) break;
+            const int nr = lane < nrows ? (u + cap - 1) / cap : 0;
+            int incl = nr;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += y;
+            }
+            const int first = incl - nr;
+            if (lane < nrows && first <= g && g < incl) {   // the lane of this block's row
+                const int k = g - first, q_u = u / nr, r_u = u % nr;
+                us.run[0] = lane;
+                us.run[1] = k * q_u + (k < r_u ? k : r_u);  // first unit
+                us.run[2] = q_u + (k < r_u ? 1 : 0);        // units
+                us.run[3] = k == nr - 1;                    // the row's last run
+                us.run_len = Lr;
+            }
+            if (lane == 63) us.run[4] = incl;               // runs in all
+        }
+        __syncthreads();
+    } else {
+        int64_t Lr = 0;
+        int u = 0;
+        if (tid < nrows) {
+            Lr = row_len(a.rows, tid, 0);
+            const int64_t ur = (Lr + kUnitKeys - 1) / kUnitKeys;
+            u = ur < 1 ? 1 : (int)ur;
+        }
+        auto block_sum = [&](int x) {                  // block sum of x (uniform result)
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+            __syncthreads();                           // earlier readers of us.part are done
+            if (lane == 0) us.part[wave] = x;
+            __syncthreads();
+            int t = 0;
+#pragma unroll
+            for (int w = 0; w < kDmaThreads / 64; w++) t += us.part[w];
+            return t;
+        };
+        int cap = (block_sum(u) + G - 1) / G;
+        for (;; cap++) {                               // ends by cap = max u_r (then nrows <= G runs)
+            const int n = tid < nrows ? (u + cap - 1) / cap : 0;
+            if (block_sum(n) <= G) break;
+        }
+        const int nr = tid < nrows ? (u + cap - 1) / cap : 0;   // this row's runs
+        int incl = nr;                                 // inclusive scan of nr over the rows
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += y;
+        }
+        __syncthreads();
+        if (lane == 63) us.part[wave] = incl;
+        __syncthreads();
+        int base = 0;
+#pragma unroll
+        for (int w = 0; w < kDmaThreads / 64; w++) base += w < wave ? us.part[w] : 0;
+        const int first = base + incl - nr;
+        if (tid < nrows && first <= g && g < first + nr) {
+            const int k = g - first, q_u = u / nr, r_u = u % nr;
+            us.run[0] = tid;
+            us.run[1] = k * q_u + (k < r_u ? k : r_u);
+            us.run[2] = q_u + (k < r_u ? 1 : 0);
+            us.run[3] = k == nr - 1;
+            us.run_len = Lr;
+        }
+        if (tid == nrows - 1) us.run[4] = first + nr;
+        __syncthreads();
+    }
+    if (g >= us.run[4]) return;                        // more blocks than runs
+    const int row = __builtin_amdgcn_readfirstlane(us.run[0]);
+    const int64_t blk0 = (int64_t)kUnitKeys * __builtin_amdgcn_readfirstlane(us.run[1]);
+    const int64_t span = (int64_t)kUnitKeys * __builtin_amdgcn_readfirstlane(us.run[2]);
+    const bool last_run = __builtin_amdgcn_readfirstlane(us.run[3]) != 0;
+    const int64_t Lrow = us.run_len;
+    // ---- the run: row `row`, keys [blk0, blk0 + span)
+    const int qrow = row;
+    const int b = row;
+    const int64_t T = a.rows.T;
+    const int64_t L = Lrow;
+    float *out = a.scores + (int64_t)qrow * T;
+    const int64_t end = last_run ? T : blk0 + span;    // the slots this block answers for
+    const bool loader = wave >= kDmaComputeWaves;
+    const int head = tid >> 3, sub = tid & 7;
+    const bool rope_on = a.rope_cos != nullptr;
+    if (blk0 >= L) {                                   // an empty row: -inf (and its quantized query)
+        if (loader) return;
+        for (int64_t s = blk0 + tid; s < end && s < T; s += 64 * kDmaComputeWaves) out[s] = -__builtin_inff();
+        if (blk0 == 0 && a.q_fp8_out) {
+            const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
+            const uint4 q0 = qs[0], q1 = qs[1];
+            uint32_t in[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+            if (rope_on) {
+                Rope16 rr;
+                load_rope16(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2), a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), sub, rr);
+                rope_row16(in, rr, sub);
+            }
+            uint32_t codes[4];
+            int j;
+            quantize_row16(in, codes, j);
+            *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) =
+                make_uint4(codes[0], codes[1], codes[2], codes[3]);
+            if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = fold_weight(a.w[(int64_t)qrow * LK_HEADS + head], j);
+        }
+        return;
+    }
+    const uint8_t *kbase = a.k_cache + (int64_t)b * a.cache_seq_stride * LK_DIM;
+    // units holding a valid key (uniform, >= 1 here); the slots past them are only -inf
+    const int nunits = (int)((L - blk0 < span ? L - blk0 + kUnitKeys - 1 : span) / kUnitKeys);
+    const int NP = kUnitTiles * nunits;                // phases: one tile of every compute wave each
+    if (loader) {
+        // Loader wave v: in phase P (tile P % 2 of unit P / 2), DMA instruction i covers
+        // phase rows 8 (v * kDmaPerPhase + i) .. +7; phase P lands in buffer P % 4.
+        const int v = wave - kDmaComputeWaves;
+        auto issue_phase = [&](int P) {
+            const int p = P & (kUnitTiles - 1);
+            const int64_t ub = blk0 + (int64_t)kUnitKeys * (P / kUnitTiles);
+            uint8_t *buf = sm.k + (P & (kDecTiles - 1)) * kDmaPhaseBytes;
+#pragma unroll
+            for (int i = 0; i < kDmaPerPhase; i++) {
+                const int R = 8 * (v * kDmaPerPhase + i) + (lane >> 3);   // row within the phase
+                const int w = R >> 5, r = R & 31;
+                const int q = kslot(r, lane & 7);                         // the chunk this lane's slot holds
+                const int64_t s = ub + 64 * w + 32 * p + r;
+                const uint8_t *src = kbase + (s < L ? s : 0) * LK_DIM + 16 * q;
+                dma_b128(src, buf + 1024 * (v * kDmaPerPhase + i));
+            }
+        };
+        issue_phase(0);
+        issue_phase(1);                                // NP >= 2
+#pragma unroll 1
+        for (int P = 0; P < NP; P++) {                 // one barrier per phase, as the compute waves
+            if (P + 1 < NP) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerPhase));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __syncthreads();                           // phase P landed (P = 0: and the query is prepared)
+            if (P + 2 < NP) issue_phase(P + 2);        // into the buffer of phase P - 2, read before barrier P
+        }
+        return;
+    }
+
+    // Compute wave `wave`: in unit j, keys blk0 + 512 j + 64 wave .. + 63 (tile p: + 32 p).
+    const int64_t pn = L - 1 < blk0 + span ? L - 1 : -1;   // the new key's slot (uniform)
+    const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
+    const uint4 qp0 = qs[0], qp1 = qs[1];
+    const float wr = a.w[(int64_t)qrow * LK_HEADS + head];
+    const uint32_t kn = reinterpret_cast<const uint32_t *>(a.k_new + (int64_t)b * LK_DIM)[lane];
+    const float *kc_row = rope_on ? a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
+    const float *ks_row = rope_on ? a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
+    const float2 krc = reinterpret_cast<const float2 *>(kc_row)[lane & 15];
+    const float2 krs = reinterpret_cast<const float2 *>(ks_row)[lane & 15];
+    Rope32 rope_row;
+    if (rope_on)
+        load_rope32_uniform(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2),
+                            a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), rope_row);
+    const float *sbase = a.k_scale + (int64_t)b * a.cache_seq_stride;
+    float ks_u;                                        // key scale of this lane's key in the current unit
+    {
+        const int64_t s = blk0 + 64 * wave + lane;
+        ks_u = sbase[s < L ? s : 0];
+    }
+    {
+        uint32_t in[8] = {qp0.x, qp0.y, qp0.z, qp0.w, qp1.x, qp1.y, qp1.z, qp1.w};
+        if (rope_on) {
+            Rope16 rope;
+            pick_rope16(rope_row, sub, rope);
+            rope_row16(in, rope, sub);
+        }
+        uint32_t codes[4];
+        int j;
+        quantize_row16(in, codes, j);
+        const uint4 piece = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+        *reinterpret_cast<uint4 *>(sq + head * kQPitch + 16 * sub) = piece;
+        const float we = fold_weight(wr, j);
+        if (sub == 0) sw[head] = we;
+        if (blk0 == 0 && a.q_fp8_out) {
+            *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) = piece;
+            if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = we;
+        }
+    }
+    if (pn >= 0 && wave == 0) {                        // the new key, spread over wave 0 (2 features a lane)
+        uint32_t kin = kn;
+        if (rope_on) rope_row_wave(kin, krc, krs);
+        int kj;
+        const uint32_t kc = quantize_row_wave(kin, kj);
+        const int64_t row_off = (int64_t)b * a.cache_seq_stride + pn;
+        reinterpret_cast<uint16_t *>(a.k_cache + row_off * LK_DIM)[lane] = (uint16_t)kc;
+        reinterpret_cast<uint16_t *>(snew)[lane] = (uint16_t)kc;
+        if (lane == 0) {
+            const float ksc = __builtin_ldexpf(1.0f, kj);
+            a.k_scale[row_off] = ksc;
+            sm.d.snew_scale = ksc;
+        }
+    }
+    __syncthreads();                                   // query prepared, phase 0 landed
+    QueryRaw raw;
+    {
+        const int r = lane & 31, hh = lane >> 5;
+#pragma unroll
+        for (int m = 0; m < 2; m++) {
+            const uint8_t *qr = sq + (32 * m + r) * kQPitch + 64 * hh;
+#pragma unroll
+            for (int c = 0; c < 4; c++) raw.q[m][c] = *reinterpret_cast<const uint4 *>(qr + 16 * c);
+#pragma unroll
+            for (int gq = 0; gq < 4; gq++) raw.w[m][gq] = *reinterpret_cast<const float4 *>(sw + 32 * m + 8 * gq + 4 * hh);
+        }
+    }
+    QueryFrag f;
+    convert_query(raw, f);
+    // The lane-derived LDS addresses are recomputed where they are used: held across the
+    // unit loop they would not fit the register budget.
+    auto opaque_lane = [&]() {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        return ln;
+    };
+    // relu_weighted_sum with the weights read from LDS two quads at a time, in its order.
+    auto relu_weighted_sum_lds = [&](const float16v (&acc2)[2]) {
+        const int hh = opaque_lane() >> 5;
+        float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i0 = 0; i0 < 8; i0 += 2) {
+            float4 wq[2];
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int m = (i0 + i) >> 2, gq = (i0 + i) & 3;
+                wq[i] = *reinterpret_cast<const float4 *>(sw + 32 * m + 8 * gq + 4 * hh);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int m = (i0 + i) >> 2, gq = (i0 + i) & 3;
+                const float wg[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+#pragma unroll
+                for (int kk = 0; kk < 4; kk++)
+                    s4[kk] = __builtin_fmaf(__builtin_fmaxf(acc2[m][4 * gq + kk], 0.0f), wg[kk], s4[kk]);
+            }
+        }
+        return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    };
+    // Phase P's tile of this wave: its 32 keys from buffer P % 4 through the MFMAs.
+    auto tile = [&](int P, int64_t kj, int p, float16v (&accd)[2]) {
+        const int ln = opaque_lane();
+        const int r = ln & 31, hh = ln >> 5;
+        uint4 kv[4];
+        const uint8_t *rowp = sm.k + (P & (kDecTiles - 1)) * kDmaPhaseBytes + (32 * wave + r) * LK_DIM;
+#pragma unroll
+        for (int c = 0; c < 4; c++) kv[c] = *reinterpret_cast<const uint4 *>(rowp + 16 * kslot(r, 4 * hh + c));
+        const bool mine = kj + 32 * p + r == pn;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const uint4 n = snew[4 * hh + c];
+            kv[c].x = mine ? n.x : kv[c].x;
+            kv[c].y = mine ? n.y : kv[c].y;
+            kv[c].z = mine ? n.z : kv[c].z;
+            kv[c].w = mine ? n.w : kv[c].w;
+        }
+        mfma_tile(kv, f, accd);
+    };
+    const float nscale = sm.d.snew_scale;
+    float16v acc[2][2];
+#pragma unroll 1
+    for (int j = 0; j < nunits; j++) {
+        const int64_t kj = blk0 + (int64_t)kUnitKeys * j + 64 * wave;
+        if (j > 0) __syncthreads();                    // phase 2 j landed
+        tile(2 * j, kj, 0, acc[0]);
+        float ks_next = 0.0f;
+        if (j + 1 < nunits) {                          // the next unit's key scale
+            const int64_t s = kj + kUnitKeys + lane;
+            ks_next = sbase[s < L ? s : 0];
+        }
+        __syncthreads();                               // phase 2 j + 1 landed
+        tile(2 * j + 1, kj, 1, acc[1]);
+        const float p0 = relu_weighted_sum_lds(acc[0]);
+        const float sum = halves_sum_pair(p0, relu_weighted_sum_lds(acc[1]));
+        const int64_t s = kj + lane;                   // lanes 0-31: tile 0's keys, 32-63: tile 1's
+        const float ksv = s == pn ? nscale : ks_u;
+        const float v = s < L ? sum * ksv : -__builtin_inff();
+        if (s < T) out[s] = v;
+        ks_u = ks_next;
+    }
+    for (int64_t s = blk0 + (int64_t)kUnitKeys * nunits + tid; s < end && s < T; s += 64 * kDmaComputeWaves)
+        out[s] = -__builtin_inff();
+}
+
 // ------------------------------------------------------------------ decode, standalone score
 // lk_index_score with S == 1 and a prepared query: one block per (row, 1024-key block),
 // four waves (one per SIMD), each scoring 256 consecutive keys as 8 tiles through
@@ -1044,6 +1386,11 @@ hipError_t launch_decode_grid(const DecodeArgs &a, hipStream_t stream) {
     const int64_t nrows = (int64_t)rows.B * rows.S;
     const int cus = cu_count();
     if (nrows <= kPersistMaxRows && nblk * nrows * 4 > (int64_t)cus * 5) {
+        if constexpr (kFused) {                        // S == 1: runs of 512-key units, one per block
+            static_assert(kUnitMaxRows >= kPersistMaxRows, "the unit schedule takes every such row");
+            const unsigned grid = (unsigned)(nrows > cus ? nrows : cus);
+            return launch(decode_units_kernel, dim3(grid), dim3(kDmaThreads), 0u, stream, a);
+        }
         const unsigned grid = (unsigned)(nblk * nrows < cus ? nblk * nrows : cus);
         return launch(decode_persistent_kernel<kFused>, dim3(grid), dim3(kDecThreads), 0u, stream, a);
     }
