@@ -116,29 +116,14 @@ __device__ __forceinline__ void mfma_tile(const uint4 (&kv)[4], const QueryFrag 
 // j + kFly (load_tile(j + kFly)), kFly steps before it is needed.  Two tiles make 64
 // keys, one per lane after a cross-half swap (lanes 0-31: tile 2p, lanes 32-63: tile
 // 2p + 1 -> key key0 + 64 p + lane), scaled by ks[p] and stored (-inf past the valid
-// prefix L, nothing past T).  kNewKey: the lane holding key `pn` (-1: none) takes its
-// operand from `nk` (LDS: the new key's 128 codes, 64 bytes per lane half) in place of
-// the row it loaded (a select, so the steps stay free of branches).
-template <int kTiles, int kFly, bool kNewKey, typename LoadTile>
+// prefix L, nothing past T).
+template <int kTiles, int kFly, typename LoadTile>
 __device__ __forceinline__ void pipelined_tiles(uint4 (&kv)[kTiles][4], LoadTile load_tile, const QueryFrag &f,
-                                                const float (&ks)[kTiles / 2], int64_t key0, int64_t pn,
-                                                const uint4 *nk, int64_t T, int64_t L, float *out) {
+                                                const float (&ks)[kTiles / 2], int64_t key0, int64_t T, int64_t L,
+                                                float *out) {
     static_assert(kTiles % 2 == 0 && kFly >= 1 && kFly <= kTiles, "tile schedule");
-    const int lane = __lane_id(), r = lane & 31;
-    auto start_tile = [&](int j, float16v (&acc)[2]) {
-        if constexpr (kNewKey) {
-            const bool mine = key0 + 32 * j + r == pn;
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const uint4 n = nk[4 * (lane >> 5) + c];
-                kv[j][c].x = mine ? n.x : kv[j][c].x;
-                kv[j][c].y = mine ? n.y : kv[j][c].y;
-                kv[j][c].z = mine ? n.z : kv[j][c].z;
-                kv[j][c].w = mine ? n.w : kv[j][c].w;
-            }
-        }
-        mfma_tile(kv[j], f, acc);
-    };
+    const int lane = __lane_id();
+    auto start_tile = [&](int j, float16v (&acc)[2]) { mfma_tile(kv[j], f, acc); };
     float16v acc[2][2];
     float part[2];
     start_tile(0, acc[0]);
@@ -230,16 +215,14 @@ struct DecodeShared {
     float snew_scale;
 };
 
-// Keys [blk0, blk0 + kDecKeysPerBlock) of score row qrow (one block's work item).
-// prep: bring in (fused: quantize) the row's query; otherwise sq and sw already hold
-// this row's query from the block's previous item.  `first`: the block's first item (a
-// later item that rewrites sq waits for every wave to be done with it).
-template <bool kFused>
+// Keys [blk0, blk0 + kDecKeysPerBlock) of score row qrow (one block's work item), from
+// the prepared query.  prep: bring the row's query into LDS; otherwise sq and sw already
+// hold it from the block's previous item.  `first`: the block's first item (a later
+// item that rewrites sq waits for every wave to be done with it).
 __device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &sm, int qrow, int64_t blk0,
                                             bool prep, bool first) {
     uint8_t *const sq = sm.sq;
     float *const sw = sm.sw;
-    uint4 *const snew = sm.snew;
     const int lane = __lane_id();
     const int wave = threadIdx.x >> 6;
     const int b = qrow / a.rows.S;
@@ -248,66 +231,20 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &s
     const int64_t L = row_len(a.rows, b, t);
     const int64_t key0 = blk0 + (int64_t)wave * kDecKeysPerWave;
     float *out = a.scores + (int64_t)qrow * T;
-    const int head = threadIdx.x >> 3, sub = threadIdx.x & 7;   // fused: this thread's 16 features of a head
     if (blk0 >= L) {                                   // the whole block is masked: -inf only
         for (int64_t s = blk0 + threadIdx.x; s < blk0 + kDecKeysPerBlock && s < T; s += kDecThreads)
             out[s] = -__builtin_inff();
-        if constexpr (kFused) {                        // a row with L == 0 still returns its quantized query
-            if (blk0 == 0 && a.q_fp8_out) {
-                const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
-                const uint4 q0 = qs[0], q1 = qs[1];
-                uint32_t in[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-                if (a.rope_cos) {
-                    Rope16 rr;
-                    load_rope16(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2), a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), sub, rr);
-                    rope_row16(in, rr, sub);
-                }
-                uint32_t codes[4];
-                int j;
-                quantize_row16(in, codes, j);
-                *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) =
-                    make_uint4(codes[0], codes[1], codes[2], codes[3]);
-                if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = fold_weight(a.w[(int64_t)qrow * LK_HEADS + head], j);
-            }
-        }
         return;
     }
     const int r = lane & 31, hh = lane >> 5;
-    // fused: the new key's slot when this block holds it, else -1 (uniform)
-    const int64_t pn = (kFused && L - 1 < blk0 + kDecKeysPerBlock) ? L - 1 : -1;
 
     if (prep && !first) __syncthreads();               // every wave has its A fragments of the last row
-    // Query, weights and (fused) new-key loads, issued before the K loads and never
-    // under a branch, so the waits of the staging below count the K loads exactly.
-    // (An item that reuses the row's query still issues them; they are small.)
-    uint4 qp0, qp1;
-    uint32_t kn = 0;                                   // fused: new-key features 2 lane, 2 lane + 1
-    float2 krc = {0.f, 0.f}, krs = {0.f, 0.f};         // fused: their RoPE table entries
-    float4 wv;
-    float wr = 0.f;
-    Rope32 rope_row;                                   // fused: the token's RoPE table row (scalar loads)
-    if constexpr (kFused) {
-        const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
-        qp0 = qs[0];
-        qp1 = qs[1];
-        wr = a.w[(int64_t)qrow * LK_HEADS + head];
-        kn = reinterpret_cast<const uint32_t *>(a.k_new + (int64_t)b * LK_DIM)[lane];
-        // The new key's table entries are loaded whether or not RoPE is on (a load
-        // under a branch would be waited for with all later loads); without tables
-        // they come from the key row itself and are ignored.
-        const bool rope_on = a.rope_cos != nullptr;
-        const float *kc_row = rope_on ? a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
-        const float *ks_row = rope_on ? a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
-        krc = reinterpret_cast<const float2 *>(kc_row)[lane & 15];
-        krs = reinterpret_cast<const float2 *>(ks_row)[lane & 15];
-        if (rope_on)                                   // the step's token: shared by the query and the new key
-            load_rope32_uniform(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2),
-                                a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), rope_row);
-    } else {
-        qp0 = reinterpret_cast<const uint4 *>(a.q_fp8 + (int64_t)qrow * LK_HEADS * LK_DIM)[threadIdx.x];
-        // Every thread loads and stores a float4 of the weights (lane % 16 picks which).
-        wv = reinterpret_cast<const float4 *>(a.w_eff + (int64_t)qrow * LK_HEADS)[lane & 15];
-    }
+    // Query and weight loads, issued before the K loads and never under a branch, so the
+    // waits of the staging below count the K loads exactly.  (An item that reuses the
+    // row's query still issues them; they are small.)
+    const uint4 qp0 = reinterpret_cast<const uint4 *>(a.q_fp8 + (int64_t)qrow * LK_HEADS * LK_DIM)[threadIdx.x];
+    // Every thread loads and stores a float4 of the weights (lane % 16 picks which).
+    const float4 wv = reinterpret_cast<const float4 *>(a.w_eff + (int64_t)qrow * LK_HEADS)[lane & 15];
     // Key scales before the K loads: the first tile pair's store needs them, and a
     // load issued after the K loads could only be waited for together with all of K.
     float ks[kDecTiles / 2];
@@ -324,49 +261,15 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &s
 #pragma unroll
         for (int c = 0; c < 4; c++) kv[j][c] = src[c];       // rows past L re-read row 0 (masked below)
     };
-    // Half of the wave's K tiles are issued before the query preparation, the other
-    // half inside the tile pipeline, two steps ahead of their use: issuing all of them
-    // first left waves queued behind the address pipeline before their preparation
-    // could start, and issuing the second half right after it delayed the first MFMAs.
+    // Half of the wave's K tiles are issued before the query staging, the other half
+    // inside the tile pipeline, two steps ahead of their use: issuing all of them first
+    // left waves queued behind the address pipeline before their staging could start,
+    // and issuing the second half right after it delayed the first MFMAs.
 #pragma unroll
     for (int j = 0; j < kDecFly; j++) load_tile(j);
     // Keep these loads above this point, ahead of the staging and its waits.
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kFused) {
-      if (prep) {
-        uint32_t in[8] = {qp0.x, qp0.y, qp0.z, qp0.w, qp1.x, qp1.y, qp1.z, qp1.w};
-        Rope16 rope;
-        if (a.rope_cos) {
-            pick_rope16(rope_row, sub, rope);
-            rope_row16(in, rope, sub);
-        }
-        uint32_t codes[4];
-        int j;
-        quantize_row16(in, codes, j);
-        const uint4 piece = make_uint4(codes[0], codes[1], codes[2], codes[3]);
-        *reinterpret_cast<uint4 *>(sq + head * kQPitch + 16 * sub) = piece;
-        const float we = fold_weight(wr, j);
-        if (sub == 0) sw[head] = we;
-        if (blk0 == 0 && a.q_fp8_out) {
-            *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) = piece;
-            if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = we;
-        }
-      }
-        if (pn >= 0 && wave == 0) {                    // the new key, spread over wave 0 (2 features a lane)
-            uint32_t kin = kn;
-            if (a.rope_cos) rope_row_wave(kin, krc, krs);
-            int kj;
-            const uint32_t kc = quantize_row_wave(kin, kj);
-            const int64_t row = (int64_t)b * a.cache_seq_stride + pn;
-            reinterpret_cast<uint16_t *>(a.k_cache + row * LK_DIM)[lane] = (uint16_t)kc;
-            reinterpret_cast<uint16_t *>(snew)[lane] = (uint16_t)kc;
-            if (lane == 0) {
-                const float ksc = __builtin_ldexpf(1.0f, kj);
-                a.k_scale[row] = ksc;
-                sm.snew_scale = ksc;
-            }
-        }
-    } else if (prep) {
+    if (prep) {
         const int piece = threadIdx.x;                 // head piece / 8, 16-byte chunk piece % 8
         *reinterpret_cast<uint4 *>(sq + (piece >> 3) * kQPitch + 16 * (piece & 7)) = qp0;
         reinterpret_cast<float4 *>(sw)[lane & 15] = wv;    // duplicate stores of equal values
@@ -386,13 +289,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &s
     }
     QueryFrag f;
     convert_query(raw, f);
-    // fused: the lanes of slot pn take the fresh codes and scale (unused when pn < 0)
-    if constexpr (kFused) {
-        const float nscale = sm.snew_scale;
-#pragma unroll
-        for (int p = 0; p < kDecTiles / 2; p++) ks[p] = key0 + 64 * p + lane == pn ? nscale : ks[p];
-    }
-    pipelined_tiles<kDecTiles, kDecFly, kFused>(kv, load_tile, f, ks, key0, pn, snew, T, L, out);
+    pipelined_tiles<kDecTiles, kDecFly>(kv, load_tile, f, ks, key0, T, L, out);
 }
 
 // ------------------------------------------------------------------ decode, fused step
@@ -1061,18 +958,17 @@ __global__ void __launch_bounds__(kPipeThreads) decode_pipe_kernel(DecodeArgs a)
     }
     QueryFrag f;
     convert_query(raw, f);
-    pipelined_tiles<kPipeTiles, kPipeFly, false>(kv, load_tile, f, ks, key0, -1, nullptr, T, L, out);
+    pipelined_tiles<kPipeTiles, kPipeFly>(kv, load_tile, f, ks, key0, T, L, out);
 }
 
-// Grids of more items than the chip runs at once (many rows, or ragged rows whose key
-// blocks mostly end early): a block per compute unit walks a contiguous range of the
-// valid items, in row order, so it quantizes each row's query once for all of its
+// lk_index_score over more items than the chip runs at once (many rows, or ragged rows
+// whose key blocks mostly end early): a block per compute unit walks a contiguous range
+// of the valid items, in row order, so it stages each row's query once for all of its
 // items of that row, and items of different lengths even out across blocks.  Every
 // block derives the same schedule from the row lengths: row r has
-// ceil(L_r / kDecKeysPerBlock) items (one for a row with L_r = 0 when the quantized
-// query is requested), and the key blocks past them are swept to -inf by block r % grid.
+// ceil(L_r / kDecKeysPerBlock) items, and the key blocks past them are swept to -inf by
+// block r % grid.
 constexpr int kPersistMaxRows = kDecThreads;
-template <bool kFused>
 __global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) DecodeShared sm;
     __shared__ int32_t first_item[kPersistMaxRows + 1];   // row r's items: first_item[r] .. first_item[r+1]-1
@@ -1084,7 +980,6 @@ __global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeAr
     if (tid < nrows) {
         const int64_t L = row_len(a.rows, tid / a.rows.S, tid % a.rows.S);
         nv = (int)((L + kDecKeysPerBlock - 1) / kDecKeysPerBlock);
-        if (kFused && L == 0 && a.q_fp8_out) nv = 1;
     }
     // exclusive scan of nv over the rows (one per thread)
     int incl = nv;
@@ -1128,7 +1023,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeAr
         row = __builtin_amdgcn_readfirstlane(row);
         const int item0 = __builtin_amdgcn_readfirstlane(first_item[row]);
         const int64_t blk0 = (int64_t)(it - item0) * kDecKeysPerBlock;
-        decode_item<kFused>(a, sm, row, blk0, row != prev, it == i0);
+        decode_item(a, sm, row, blk0, row != prev, it == i0);
         prev = row;
     }
 }
@@ -1390,9 +1285,10 @@ hipError_t launch_decode_grid(const DecodeArgs &a, hipStream_t stream) {
             static_assert(kUnitMaxRows >= kPersistMaxRows, "the unit schedule takes every such row");
             const unsigned grid = (unsigned)(nrows > cus ? nrows : cus);
             return launch(decode_units_kernel, dim3(grid), dim3(kDmaThreads), 0u, stream, a);
+        } else {
+            const unsigned grid = (unsigned)(nblk * nrows < cus ? nblk * nrows : cus);
+            return launch(decode_persistent_kernel, dim3(grid), dim3(kDecThreads), 0u, stream, a);
         }
-        const unsigned grid = (unsigned)(nblk * nrows < cus ? nblk * nrows : cus);
-        return launch(decode_persistent_kernel<kFused>, dim3(grid), dim3(kDecThreads), 0u, stream, a);
     }
     dim3 grid((unsigned)nblk, (unsigned)rows.B);
     if constexpr (kFused) return launch(decode_kernel<false>, grid, dim3(kDmaThreads), 0u, stream, a);
