@@ -1030,7 +1030,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeAr
 
 // ------------------------------------------------------------------ prefill (S > 1)
 // A block of 8 waves (two per SIMD) owns 8 consecutive query tokens of one sequence (one
-// per wave) and a slice of up to 4096 keys, taken as chunks of 256.  Each chunk is read
+// per wave) and a slice of keys (the group's whole key range when the token groups fill
+// the chip, else up to 4096 keys), taken as chunks of 256.  Each chunk is read
 // from HBM once per block, converted to f16 once and kept in LDS (two 68 KB buffers),
 // where every wave streams it through the MFMA against its own query held in registers;
 // the chunks are double buffered, so one barrier per chunk (eight tiles per wave)
@@ -1054,8 +1055,8 @@ constexpr int kPreWaves = 8;                          // query tokens per block,
 constexpr int kPreThreads = 64 * kPreWaves;
 constexpr int kPreChunk = 256;                        // keys per LDS buffer
 constexpr int kPreTiles = kPreChunk / 32;
-constexpr int kPreChunks = 16;                        // chunks per slice
-constexpr int kPreSlice = kPreChunk * kPreChunks;     // keys per work item
+constexpr int kPreChunks = 16;                        // chunks per slice when rows are split
+constexpr int kPreSlice = kPreChunk * kPreChunks;     // keys per work item when rows are split
 constexpr int kPreRowBytes = 2 * LK_DIM + 16;         // f16 row + 16 B pad against bank conflicts
 constexpr int kPreRowGroups = kPreChunk / 32;         // 32-row groups of a chunk
 constexpr int kPrePieces = 2 * kPreWaves / kPreRowGroups;   // pieces each key row is staged in
@@ -1099,14 +1100,27 @@ __device__ __forceinline__ void store_chunk_part(uint8_t *sk, float *sks, const 
     if (threadIdx.x < kPreChunk) sks[threadIdx.x] = p.ks;
 }
 
-// Work items of the prefill grid (see above).
+int cu_count();
+
+// Work items of the prefill grid (see above).  When the token groups alone give every
+// compute unit at least two blocks, a block takes its group's whole key range (one
+// slice), so the query load, the first chunk's staging and the pipeline fill happen
+// once per group; otherwise rows are split into slices of kPreSlice keys.
 struct PrefillGrid {
     int nslices, nrg, n_items;
+    int slice_chunks;                                 // chunks per slice
+    int64_t slice_keys;                               // slice_chunks * kPreChunk
 };
 PrefillGrid prefill_grid(const RowsDev &rows) {
     PrefillGrid g;
-    g.nslices = (int)((rows.T + kPreSlice - 1) / kPreSlice);
     g.nrg = (rows.S + kPreWaves - 1) / kPreWaves;
+    const int64_t tchunks = (rows.T + kPreChunk - 1) / kPreChunk;
+    const int64_t groups = (int64_t)rows.B * g.nrg;
+    int64_t sc = kPreChunks;
+    if (groups >= 2 * (int64_t)cu_count() && tchunks > sc && tchunks <= (1 << 24)) sc = tchunks;
+    g.slice_chunks = (int)sc;
+    g.slice_keys = sc * kPreChunk;
+    g.nslices = (int)((rows.T + g.slice_keys - 1) / g.slice_keys);
     g.n_items = g.nslices * g.nrg * rows.B;
     return g;
 }
@@ -1127,7 +1141,7 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
     const int wave = threadIdx.x >> 6;
     const int t0 = rg * kPreWaves;
     const int64_t T = rows.T;
-    const int64_t slice0 = (int64_t)slice * kPreSlice;
+    const int64_t slice0 = (int64_t)slice * grid.slice_keys;
     const int t = t0 + wave;
     const bool has_row = t < rows.S;
     const int64_t L = has_row ? row_len(rows, b, t) : 0;
@@ -1137,10 +1151,11 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
     float *out = scores + ((int64_t)b * rows.S + t) * T;
     // Chunks of the slice with any valid key for some row of the block.
     const int64_t live = Lmax - slice0;
-    const int nchunks = live <= 0 ? 0 : (live >= kPreSlice ? kPreChunks : (int)((live + kPreChunk - 1) / kPreChunk));
+    const int nchunks = live <= 0 ? 0
+                      : (live >= grid.slice_keys ? grid.slice_chunks : (int)((live + kPreChunk - 1) / kPreChunk));
     // -inf for this row's slots of the chunks no row of the block needs.
     if (has_row)
-        for (int64_t s = slice0 + (int64_t)nchunks * kPreChunk + lane; s < slice0 + kPreSlice && s < T; s += 64)
+        for (int64_t s = slice0 + (int64_t)nchunks * kPreChunk + lane; s < slice0 + grid.slice_keys && s < T; s += 64)
             out[s] = -__builtin_inff();
     if (nchunks == 0) return;
     // Chunks in which every key is valid for this row: [0, nfull).

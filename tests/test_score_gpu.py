@@ -134,3 +134,29 @@ def test_score_invariants_bitwise(S):
     assert np.array_equal(s2[..., ::5], s0[..., ::5] * np.float32(2.0**-7))
     s3 = _gpu_scores(q8, np.abs(w_eff), k8, ks, T, 0, None, False)
     assert np.all(s3 >= 0)
+
+
+def test_score_whole_row_items():
+    """Prefill with enough 8-token groups (B * ceil(S / 8) >= 2 x the compute units of an
+    MI355X) that each block takes its group's whole key range: ragged lengths, causal
+    from start_pos 6000, a partial last token group and T not a multiple of 256.  Every
+    row's -inf pattern is checked against the oracle's valid length, and sampled rows
+    (both sequences, each side of the length and 8-token group edges) element by element."""
+    B, S, T, start_pos, lens = 2, 2053, 9000, 6000, [8000, 9000]
+    assert B * ((S + 7) // 8) >= 2 * 256
+    q8, w_eff, k8, ks = _quantized_inputs(31, B, S, T)
+    log(f"[score] whole-row items: B={B} S={S} T={T} start={start_pos} lens={lens}")
+    gs = _gpu_scores(q8, w_eff, k8, ks, T, start_pos, lens, True, stride_pad=5)
+    for b in range(B):
+        for t in range(S):
+            L = O.valid_len(T, lens[b], True, start_pos, t)
+            row = gs[b, t]
+            assert np.all(np.isfinite(row[:L])) and np.all(np.isneginf(row[L:])), (b, t, L)
+    samples = [0, 1, 7, 8, 1998, 1999, 2000, 2047, 2048, 2052]
+    errs = []
+    for b in range(B):
+        for t in samples:
+            L = O.valid_len(T, lens[b], True, start_pos, t)
+            ref = O.score_row(q8[b, t], w_eff[b, t], k8[b], ks[b], T, L)
+            errs.append(_check(gs[b, t][None], ref[None]))
+    log(f"[score] whole-row items: max rel err {max(errs):.2e} over {len(errs)} rows")
