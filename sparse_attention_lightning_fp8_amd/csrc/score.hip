@@ -1188,12 +1188,22 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
     };
     // The pipeline over the valid chunks.  Tiles 2i and 2i + 1 of a chunk make 64 keys
     // (lanes 0-31 and 32-63 after halves_sum_pair); the key scales of a pair are read
-    // into a register right after the previous pair's store.
+    // into a register right after the previous pair's store.  The chunk in which the
+    // row's valid prefix ends runs the same pipeline over its tile pairs up to the one
+    // holding key L - 1 (jmax tiles), with the stores masked past L and T.
     float16v acc[2][2];
     float p0 = 0.f, ks_pair = 0.f;
     int64_t s_pair = 0;
     bool owed = false;                                 // a computed tile still owes its epilogue
-    for (int c = 0; c < nfull; c++) {
+    auto store_pair = [&](float v, auto masked) {
+        const int64_t s = s_pair + lane;
+        if constexpr (decltype(masked)::value) {
+            if (s < T) out[s] = s < L ? v * ks_pair : -__builtin_inff();
+        } else {
+            out[s] = v * ks_pair;                      // s < L <= T
+        }
+    };
+    auto run_chunk = [&](int c, int jmax, auto masked) {
         const int64_t kc = slice0 + (int64_t)c * kPreChunk;
         const bool more = c + 1 < nchunks;
         if (more) load_chunk_part(kbase, sbase, kc + kPreChunk, Lmax, part);   // in flight during the MFMA work
@@ -1202,11 +1212,15 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
 #pragma unroll
         for (int j = 0; j < kPreTiles; j++) {
             __builtin_amdgcn_sched_barrier(0);
+            if (decltype(masked)::value && j >= jmax) {   // past the row's last tile pair
+                if (j == kPreStageTile && more) store_chunk_part(sk[(c + 1) & 1], sks[(c + 1) & 1], part);
+                continue;
+            }
             mfma_tile(skc, j, acc[j & 1]);
             if (owed) {                                // the epilogue of the previous tile
                 const float pv = relu_weighted_sum(acc[(j + 1) & 1], f);
                 if (j & 1) p0 = pv;                    // the previous tile is the first of a pair
-                else out[s_pair + lane] = halves_sum_pair(p0, pv) * ks_pair;   // s < L <= T
+                else store_pair(halves_sum_pair(p0, pv), masked);
             }
             if ((j & 1) == 0) {
                 ks_pair = sksc[32 * j + lane];
@@ -1238,14 +1252,28 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
         }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+    };
+    for (int c = 0; c < nfull; c++) run_chunk(c, kPreTiles, std::false_type{});
+    // The chunk holding key L - 1, if it is not a full one: its valid tile pairs.
+    int c2 = nfull;
+    if (has_row && nfull < nchunks && lrow > (int64_t)nfull * kPreChunk) {
+        const int64_t kc = slice0 + (int64_t)nfull * kPreChunk;
+        const int np = (int)((L - kc + 63) / 64);      // 1 .. kPreTiles / 2
+        run_chunk(nfull, 2 * np, std::true_type{});
+        const float pv = relu_weighted_sum(acc[1], f);  // its last tile (2 np - 1 is odd)
+        store_pair(halves_sum_pair(p0, pv), std::true_type{});
+        owed = false;
+        for (int64_t s = kc + 64 * np + lane; s < kc + kPreChunk && s < T; s += 64) out[s] = -__builtin_inff();
+        c2 = nfull + 1;
     }
     if (owed) {                                        // the last valid chunk's last tile
         const float pv = relu_weighted_sum(acc[(kPreTiles - 1) & 1], f);
-        out[s_pair + lane] = halves_sum_pair(p0, pv) * ks_pair;
+        store_pair(halves_sum_pair(p0, pv), std::false_type{});
     }
-    // Chunks that end past this row's valid length (and rows past S): one tile pair at a
-    // time, masked.  Every wave passes one barrier per chunk in either loop.
-    for (int c = nfull; c < nchunks; c++) {
+    // Chunks past the one holding key L - 1 (and every chunk of rows past S): no valid
+    // key for this row, or (rows past S) nothing to store; one tile pair at a time,
+    // masked.  Every wave passes one barrier per chunk in either loop.
+    for (int c = c2; c < nchunks; c++) {
         const int64_t kc = slice0 + (int64_t)c * kPreChunk;
         const bool more = c + 1 < nchunks;
         if (more) load_chunk_part(kbase, sbase, kc + kPreChunk, Lmax, part);
