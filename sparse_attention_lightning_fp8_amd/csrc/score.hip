@@ -1045,8 +1045,9 @@ __global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeAr
 //  - Chunks valid for the wave's row run as one software pipeline across chunk
 //    boundaries: step g issues the 16 MFMAs of tile g, then the ReLU / weight / head-sum
 //    epilogue of tile g - 1 (two tiles make 64 keys, one per lane after a cross-half
-//    swap), so the VALU epilogue runs in the shadow of the matrix core; chunks that end
-//    past the row's valid length take a plain per-pair path with the mask.
+//    swap), so the VALU epilogue runs in the shadow of the matrix core.  The chunk that
+//    holds the row's last valid key runs the same pipeline over its tile pairs up to
+//    that key, with the stores masked; later chunks of the row are only written -inf.
 //  - Work items (sequence, token group, slice) are numbered slice fastest and token
 //    groups from the last (longest causal rows first); the 1-D grid is dispatched to the
 //    8 XCDs round-robin, so block 8p + x (XCD x) takes item 8p + (x + p) % 8, which
@@ -1270,33 +1271,15 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
         const float pv = relu_weighted_sum(acc[(kPreTiles - 1) & 1], f);
         store_pair(halves_sum_pair(p0, pv), std::false_type{});
     }
-    // Chunks past the one holding key L - 1 (and every chunk of rows past S): no valid
-    // key for this row, or (rows past S) nothing to store; one tile pair at a time,
-    // masked.  Every wave passes one barrier per chunk in either loop.
+    // Chunks past the one holding key L - 1 (every chunk, for rows past S): no valid key
+    // for this row.  The wave writes them -inf, stages its share of the next chunk and
+    // passes the chunk's barrier, so every wave passes one barrier per chunk.
     for (int c = c2; c < nchunks; c++) {
         const int64_t kc = slice0 + (int64_t)c * kPreChunk;
         const bool more = c + 1 < nchunks;
         if (more) load_chunk_part(kbase, sbase, kc + kPreChunk, Lmax, part);
-        const uint8_t *skc = sk[c & 1];
-        const float *sksc = sks[c & 1];
-        if (has_row) {
-            for (int j = 0; j < kPreTiles; j += 2) {
-                if (kc + 32 * j >= L) {                // the rest of this chunk is masked for the row
-                    for (int64_t s = kc + 32 * j + lane; s < kc + kPreChunk && s < T; s += 64) out[s] = -__builtin_inff();
-                    break;
-                }
-                float partial[2];
-#pragma unroll
-                for (int jj = 0; jj < 2; jj++) {
-                    float16v a2[2];
-                    mfma_tile(skc, j + jj, a2);
-                    partial[jj] = relu_weighted_sum(a2, f);
-                }
-                const float sum = halves_sum_pair(partial[0], partial[1]);
-                const int64_t s = kc + 32 * j + lane;
-                if (s < T) out[s] = s < L ? sum * sksc[32 * j + lane] : -__builtin_inff();
-            }
-        }
+        if (has_row)
+            for (int64_t s = kc + lane; s < kc + kPreChunk && s < T; s += 64) out[s] = -__builtin_inff();
         if (more) store_chunk_part(sk[(c + 1) & 1], sks[(c + 1) & 1], part);
         __syncthreads();
     }
