@@ -60,22 +60,28 @@ class LkError(RuntimeError):
         super().__init__(f"{fn} failed: {status_string(status)} ({status})")
 
 
+def open_library(path: str) -> ctypes.CDLL:
+    """Open a build of the library at `path` with every declared signature set; raise if
+    it is not built or its ABI version differs."""
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python sparse_attention_lightning_fp8_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.lk_abi_version() != 1:
+        raise ImportError(f"{path}: unexpected ABI version {lib.lk_abi_version()}")
+    return lib
+
+
 def load() -> ctypes.CDLL:
     """Load liblk.so once; raise if it is not built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(
-                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
-                "or `python sparse_attention_lightning_fp8_amd/build.py`")
-        lib = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        if lib.lk_abi_version() != 1:
-            raise ImportError(f"{LIB_PATH}: unexpected ABI version {lib.lk_abi_version()}")
-        _lib = lib
+        _lib = open_library(LIB_PATH)
     return _lib
 
 

@@ -30,9 +30,9 @@ FILE_FLAGS = {"score.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form
               "mla.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, out_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -43,17 +43,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build() -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(out_dir: str = BUILD_DIR, lib_path: str = LIB_PATH, extra=()) -> str:
+    os.makedirs(out_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, out_dir, extra), SOURCES))
+    tmp = lib_path + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+# Debug build: every kernel fills its shared memory with 0xFF bytes (NaN as float32, f16
+# and e4m3fn) before first use, so a read of LDS that no thread wrote shows up in the
+# GPU tests that compare this build's outputs with the library's, bit for bit.
+POISON_BUILD_DIR = os.path.join(PKG, "_build_lds_poison")
+POISON_LIB_PATH = os.path.join(PKG, "liblk_lds_poison.so")
+
+
+def build_lds_poison() -> str:
+    return build(POISON_BUILD_DIR, POISON_LIB_PATH, ["-DLK_POISON_LDS"])
 
 
 # Host-side AddressSanitizer / UndefinedBehaviorSanitizer build (device code as

@@ -110,6 +110,30 @@ struct LaunchEvents {
 };
 LaunchEvents &armed_events();
 
+// Debug builds (-DLK_POISON_LDS) fill a kernel's shared objects with 0xFF bytes -- NaN as
+// float32, f16 and e4m3fn -- before their first use, so that a read of LDS no thread has
+// written turns into a parity failure.  Every thread of the block takes part and the
+// fill ends with a barrier, so the call comes first in the kernel, ahead of any return.
+#ifdef LK_POISON_LDS
+__device__ __forceinline__ void poison_lds_bytes(void *p, size_t n) {
+    if ((reinterpret_cast<uintptr_t>(p) & 3) == 0) {
+        uint32_t *w = static_cast<uint32_t *>(p);
+        for (size_t i = threadIdx.x; i < n / 4; i += blockDim.x) w[i] = 0xFFFFFFFFu;
+        for (size_t i = n / 4 * 4 + threadIdx.x; i < n; i += blockDim.x) static_cast<uint8_t *>(p)[i] = 0xFF;
+    } else {
+        for (size_t i = threadIdx.x; i < n; i += blockDim.x) static_cast<uint8_t *>(p)[i] = 0xFF;
+    }
+}
+template <typename... Objs>
+__device__ __forceinline__ void poison_lds(Objs &...objs) {
+    (poison_lds_bytes(static_cast<void *>(&objs), sizeof(objs)), ...);
+    __syncthreads();
+}
+#define LK_POISON_LDS_OBJS(...) ::lk::poison_lds(__VA_ARGS__)
+#else
+#define LK_POISON_LDS_OBJS(...) ((void)0)
+#endif
+
 // Launch on `stream`; if events are armed, they are recorded at the kernel's own start
 // and end (hipExtLaunchKernel) and disarmed.  Returns the status of this launch call
 // itself (not an error left pending by earlier, unrelated HIP calls).  The arguments

@@ -456,6 +456,7 @@ __device__ __forceinline__ int xcd_local_block() {
 // Logical block (b, head half, split), split fastest.
 __global__ void __launch_bounds__(kThreads) mla_split_kernel(MlaArgs a) {
     __shared__ __attribute__((aligned(16))) SharedMem sm;
+    LK_POISON_LDS_OBJS(sm);
     SplitCtx x;
     const int id = xcd_local_block();
     x.split = id % a.nsplit;

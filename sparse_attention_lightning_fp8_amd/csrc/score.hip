@@ -334,6 +334,7 @@ template <bool kSelect>
 __global__ void __launch_bounds__(kDmaThreads) decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) DmaShared sm;
     __shared__ std::conditional_t<kSelect, SelectShared, char> ssel;
+    LK_POISON_LDS_OBJS(sm, ssel);
     uint8_t *const sq = sm.d.sq;
     float *const sw = sm.d.sw;
     uint4 *const snew = sm.d.snew;
@@ -579,6 +580,7 @@ struct UnitShared {
 
 __global__ void __launch_bounds__(kDmaThreads) decode_units_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) UnitShared us;
+    LK_POISON_LDS_OBJS(us);
     DmaShared &sm = us.s;
     uint8_t *const sq = sm.d.sq;
     float *const sw = sm.d.sw;
@@ -905,6 +907,7 @@ static_assert(LK_HEADS * LK_DIM / 16 == 2 * kPipeThreads, "two 16-byte query pie
 __global__ void __launch_bounds__(kPipeThreads) decode_pipe_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t sq[LK_HEADS * kQPitch];
     __shared__ __attribute__((aligned(16))) float sw[LK_HEADS];
+    LK_POISON_LDS_OBJS(sq, sw);
     const int qrow = blockIdx.y;
     const int64_t blk0 = (int64_t)blockIdx.x * kDecKeysPerBlock;
     const int lane = __lane_id(), wave = threadIdx.x >> 6;
@@ -973,6 +976,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeAr
     __shared__ __attribute__((aligned(16))) DecodeShared sm;
     __shared__ int32_t first_item[kPersistMaxRows + 1];   // row r's items: first_item[r] .. first_item[r+1]-1
     __shared__ int32_t wave_tot[kDecWaves];
+    LK_POISON_LDS_OBJS(sm, first_item, wave_tot);
     const int nrows = a.rows.B * a.rows.S;             // <= kPersistMaxRows (host check)
     const int64_t T = a.rows.T;
     const int tid = threadIdx.x, lane = __lane_id(), wave = tid >> 6;
@@ -1132,6 +1136,7 @@ score_prefill_kernel(const uint8_t *__restrict__ q_fp8, const float *__restrict_
                      int64_t cache_seq_stride, RowsDev rows, float *__restrict__ scores, PrefillGrid grid) {
     __shared__ __attribute__((aligned(16))) uint8_t sk[2][kPreChunk * kPreRowBytes];
     __shared__ float sks[2][kPreChunk];
+    LK_POISON_LDS_OBJS(sk, sks);
     const int p8 = (int)(blockIdx.x >> 3), x8 = (int)(blockIdx.x & 7);
     const int item = (p8 << 3) + ((x8 + p8) & 7);
     if (item >= grid.n_items) return;

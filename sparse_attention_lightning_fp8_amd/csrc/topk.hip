@@ -17,6 +17,7 @@ topk_kernel(const float *__restrict__ scores, RowsDev rows, int32_t k, int32_t *
     __shared__ __attribute__((aligned(16))) uint32_t cand_key[Shape<NT>::kSmall];
     __shared__ __attribute__((aligned(16))) uint32_t cand_idx[Shape<NT>::kSmall];
     __shared__ uint32_t ccount;
+    LK_POISON_LDS_OBJS(hist_buf, wtot, wsum, wred, sel, cand_key, cand_idx, ccount);
     const TopkLds<NT> sh{hist_buf, wtot, wsum, wred, sel, cand_key, cand_idx, &ccount};
     const int row = blockIdx.x;
     const int b = row / rows.S;
