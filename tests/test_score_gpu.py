@@ -160,3 +160,51 @@ def test_score_whole_row_items():
             ref = O.score_row(q8[b, t], w_eff[b, t], k8[b], ks[b], T, L)
             errs.append(_check(gs[b, t][None], ref[None]))
     log(f"[score] whole-row items: max rel err {max(errs):.2e} over {len(errs)} rows")
+
+
+def _random_code_inputs(rng, B, S, cap):
+    """Uniform finite e4m3fn codes for queries and keys, power-of-two key scales and
+    small folded weights (the score kernel's input contract, without the quantizer)."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    q8 = rng.choice(codes, (B, S, 64, 128))
+    k8 = rng.choice(codes, (B, cap, 128))
+    ks = np.exp2(rng.integers(-12, 0, (B, cap))).astype(np.float32)
+    w_eff = (rng.standard_normal((B, S, 64)) * 1e-3).astype(np.float32)
+    return q8, w_eff, k8, ks
+
+
+# Prefill grids on both sides of the whole-row threshold (B * ceil(S / 8) >= 2 x 256
+# compute units): 513, 511, 512 and 516 token groups, and a small S; T off the 64- and
+# 256-key grids; causal rows from start_pos; ragged lengths 0, 1, inside and past T.
+GRID_CASES = [
+    # name, B, S, T, start_pos, lens, causal
+    ("groups513_causal", 1, 4099, 6000, 1901, None, True),
+    ("groups511_causal", 1, 4088, 6000, 1912, None, True),
+    ("groups512_ragged", 2, 4096 // 2, 4353, 0, [0, 5000], False),
+    ("groups516_ragged_causal", 3, 1370, 5001, 3631, [1, 4999, 5001], True),
+    ("small_S_causal", 2, 9, 5000, 4991, None, True),
+]
+
+
+@pytest.mark.parametrize("name,B,S,T,start_pos,lens,causal", GRID_CASES, ids=[c[0] for c in GRID_CASES])
+def test_prefill_grid_forms(name, B, S, T, start_pos, lens, causal):
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    q8, w_eff, k8, ks = _random_code_inputs(rng, B, S, T)
+    log(f"[score] prefill grid {name}: B={B} S={S} T={T} start={start_pos} lens={lens} causal={causal}")
+    gs = _gpu_scores(q8, w_eff, k8, ks, T, start_pos, lens, causal, stride_pad=7)
+    Ls = np.empty((B, S), np.int64)
+    for b in range(B):
+        sl = max(int(lens[b]), 0) if lens is not None else -1
+        for t in range(S):
+            L = O.valid_len(T, sl, causal, start_pos, t)
+            Ls[b, t] = L
+            row = gs[b, t]
+            assert np.all(np.isfinite(row[:L])) and np.all(np.isneginf(row[L:])), (b, t, L)
+    # rows at the edges of 8-token groups, the first and last, and a few at random
+    cand = {0, 7, 8, S // 2, S - 1} | set(int(x) for x in rng.integers(0, S, 3))
+    errs = []
+    for b in range(B):
+        for t in sorted(c for c in cand if 0 <= c < S):
+            ref = O.score_row(q8[b, t], w_eff[b, t], k8[b], ks[b], T, int(Ls[b, t]))
+            errs.append(_check(gs[b, t][None], ref[None]))
+    log(f"[score] prefill grid {name}: max rel err {max(errs):.2e} over {len(errs)} rows")
