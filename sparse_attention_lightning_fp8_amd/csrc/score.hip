@@ -157,21 +157,12 @@ __device__ __forceinline__ void pipelined_tiles(uint4 (&kv)[kTiles][4], LoadTile
 //    item's keys into LDS while compute waves prepare the query; as
 //    decode_kernel<true> (lk_decode_select, rows of one item) the block also keeps
 //    its scores in LDS and its loader waves then select the row's top-k from there;
-//  - decode_units_kernel (the fused step when the items outnumber what the chip runs
-//    at once): the same loader-wave block over a balanced run of 512-key units of one
-//    row, one per compute unit;
+//  - decode_units_kernel (when the items outnumber what the chip runs at once, for the
+//    fused step and for lk_index_score alike): the same loader-wave block over a
+//    balanced run of 512-key units of one row, one per compute unit; the standalone
+//    form reads the prepared query instead of quantizing it and writes no key;
 //  - decode_pipe_kernel (lk_index_score with a prepared query, one block per item):
-//    four waves with K in registers;
-//  - decode_persistent_kernel (lk_index_score when the items outnumber what the chip
-//    runs at once): one block per compute unit walks a range of items with decode_item.
-// In decode_item, one wave scores 128 consecutive keys (4 tiles of 32) and a block of
-// kDecWaves waves covers the item.  Each lane loads its 4 x 64 bytes of K straight
-// into the B-operand registers (keys are read exactly once, so staging K in LDS brings
-// no reuse).  The query (8 KB as e4m3fn) and its weights (256 B) are needed by every
-// wave: the block fetches them once into LDS and each wave takes its A fragments from
-// there.  Order of work: the query loads, then the first kDecFly K tiles of the wave,
-// then the query staging while K streams in, then the tiles through pipelined_tiles,
-// which requests the rest of K as it goes.
+//    four waves with K in registers.
 //
 // The fused kernels (lk_decode_score) start from the bf16 query, the raw weights and
 // the new key of the decode step: each block quantizes the row's 64 query heads itself
@@ -184,7 +175,6 @@ constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecTiles = 4;                       // 32-key tiles per wave
 constexpr int kDecKeysPerWave = 32 * kDecTiles;    // 128
 constexpr int kDecKeysPerBlock = kDecKeysPerWave * kDecWaves;
-constexpr int kDecFly = kDecTiles / 2;             // tiles in flight ahead of the MFMA stream
 constexpr int kQPitch = LK_DIM + 16;               // LDS row pitch of the staged query (spreads banks)
 static_assert(LK_HEADS * LK_DIM / 16 == kDecThreads, "one 16-byte query piece per thread");
 static_assert(LK_HEADS * 8 == kDecThreads, "one 8-lane row group per head");
@@ -215,87 +205,10 @@ struct DecodeShared {
     float snew_scale;
 };
 
-// Keys [blk0, blk0 + kDecKeysPerBlock) of score row qrow (one block's work item), from
-// the prepared query.  prep: bring the row's query into LDS; otherwise sq and sw already
-// hold it from the block's previous item.  `first`: the block's first item (a later
-// item that rewrites sq waits for every wave to be done with it).
-__device__ __forceinline__ void decode_item(const DecodeArgs &a, DecodeShared &sm, int qrow, int64_t blk0,
-                                            bool prep, bool first) {
-    uint8_t *const sq = sm.sq;
-    float *const sw = sm.sw;
-    const int lane = __lane_id();
-    const int wave = threadIdx.x >> 6;
-    const int b = qrow / a.rows.S;
-    const int t = qrow - b * a.rows.S;
-    const int64_t T = a.rows.T;
-    const int64_t L = row_len(a.rows, b, t);
-    const int64_t key0 = blk0 + (int64_t)wave * kDecKeysPerWave;
-    float *out = a.scores + (int64_t)qrow * T;
-    if (blk0 >= L) {                                   // the whole block is masked: -inf only
-        for (int64_t s = blk0 + threadIdx.x; s < blk0 + kDecKeysPerBlock && s < T; s += kDecThreads)
-            out[s] = -__builtin_inff();
-        return;
-    }
-    const int r = lane & 31, hh = lane >> 5;
-
-    if (prep && !first) __syncthreads();               // every wave has its A fragments of the last row
-    // Query and weight loads, issued before the K loads and never under a branch, so the
-    // waits of the staging below count the K loads exactly.  (An item that reuses the
-    // row's query still issues them; they are small.)
-    const uint4 qp0 = reinterpret_cast<const uint4 *>(a.q_fp8 + (int64_t)qrow * LK_HEADS * LK_DIM)[threadIdx.x];
-    // Every thread loads and stores a float4 of the weights (lane % 16 picks which).
-    const float4 wv = reinterpret_cast<const float4 *>(a.w_eff + (int64_t)qrow * LK_HEADS)[lane & 15];
-    // Key scales before the K loads: the first tile pair's store needs them, and a
-    // load issued after the K loads could only be waited for together with all of K.
-    float ks[kDecTiles / 2];
-#pragma unroll
-    for (int p = 0; p < kDecTiles / 2; p++) {
-        const int64_t s = key0 + 64 * p + lane;
-        ks[p] = a.k_scale[(int64_t)b * a.cache_seq_stride + (s < L ? s : 0)];
-    }
-    const uint8_t *kbase = a.k_cache + (int64_t)b * a.cache_seq_stride * LK_DIM;
-    uint4 kv[kDecTiles][4];
-    auto load_tile = [&](int j) {
-        const int64_t s = key0 + 32 * j + r;
-        const uint4 *src = reinterpret_cast<const uint4 *>(kbase + (s < L ? s : 0) * LK_DIM + 64 * hh);
-#pragma unroll
-        for (int c = 0; c < 4; c++) kv[j][c] = src[c];       // rows past L re-read row 0 (masked below)
-    };
-    // Half of the wave's K tiles are issued before the query staging, the other half
-    // inside the tile pipeline, two steps ahead of their use: issuing all of them first
-    // left waves queued behind the address pipeline before their staging could start,
-    // and issuing the second half right after it delayed the first MFMAs.
-#pragma unroll
-    for (int j = 0; j < kDecFly; j++) load_tile(j);
-    // Keep these loads above this point, ahead of the staging and its waits.
-    __builtin_amdgcn_sched_barrier(0);
-    if (prep) {
-        const int piece = threadIdx.x;                 // head piece / 8, 16-byte chunk piece % 8
-        *reinterpret_cast<uint4 *>(sq + (piece >> 3) * kQPitch + 16 * (piece & 7)) = qp0;
-        reinterpret_cast<float4 *>(sw)[lane & 15] = wv;    // duplicate stores of equal values
-    }
-    __syncthreads();
-    // A wave whose keys are all masked still runs the tiles (on re-read row 0) and
-    // stores -inf: a branch here would let the compiler sink the K loads below the
-    // barrier.  Only blocks that straddle a row's end have such waves.
-    QueryRaw raw;
-#pragma unroll
-    for (int m = 0; m < 2; m++) {
-        const uint8_t *qr = sq + (32 * m + r) * kQPitch + 64 * hh;
-#pragma unroll
-        for (int c = 0; c < 4; c++) raw.q[m][c] = *reinterpret_cast<const uint4 *>(qr + 16 * c);
-#pragma unroll
-        for (int g = 0; g < 4; g++) raw.w[m][g] = *reinterpret_cast<const float4 *>(sw + 32 * m + 8 * g + 4 * hh);
-    }
-    QueryFrag f;
-    convert_query(raw, f);
-    pipelined_tiles<kDecTiles, kDecFly>(kv, load_tile, f, ks, key0, T, L, out);
-}
-
 // ------------------------------------------------------------------ decode, fused step
 // One block per item, K streamed into LDS by dedicated waves.  A wave that issues
 // loads stalls once the compute unit's memory queue is full (it drains at the chip's
-// HBM rate), so with K loaded into each wave's own registers (decode_item) every wave
+// HBM rate), so with K loaded into each wave's own registers every wave
 // waits behind its K loads before it can start the query preparation, which the whole
 // item then waits for.  Here four loader waves move the item's 1024 keys (128 KB)
 // into LDS with global_load_lds DMA, in four phases of 32 KB (phase p = tile p of
@@ -578,6 +491,7 @@ struct UnitShared {
     int32_t part[kDmaThreads / 64];                    // per-wave partial sums of the schedule
 };
 
+template <bool kFused>
 __global__ void __launch_bounds__(kDmaThreads) decode_units_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) UnitShared us;
     LK_POISON_LDS_OBJS(us);
@@ -696,7 +610,7 @@ __global__ void __launch_bounds__(kDmaThreads) decode_units_kernel(DecodeArgs a)
     if (blk0 >= L) {                                   // an empty row: -inf (and its quantized query)
         if (loader) return;
         for (int64_t s = blk0 + tid; s < end && s < T; s += 64 * kDmaComputeWaves) out[s] = -__builtin_inff();
-        if (blk0 == 0 && a.q_fp8_out) {
+        if (kFused && blk0 == 0 && a.q_fp8_out) {
             const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
             const uint4 q0 = qs[0], q1 = qs[1];
             uint32_t in[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
@@ -749,57 +663,68 @@ __global__ void __launch_bounds__(kDmaThreads) decode_units_kernel(DecodeArgs a)
     }
 
     // Compute wave `wave`: in unit j, keys blk0 + 512 j + 64 wave .. + 63 (tile p: + 32 p).
-    const int64_t pn = L - 1 < blk0 + span ? L - 1 : -1;   // the new key's slot (uniform)
-    const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
-    const uint4 qp0 = qs[0], qp1 = qs[1];
-    const float wr = a.w[(int64_t)qrow * LK_HEADS + head];
-    const uint32_t kn = reinterpret_cast<const uint32_t *>(a.k_new + (int64_t)b * LK_DIM)[lane];
-    const float *kc_row = rope_on ? a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
-    const float *ks_row = rope_on ? a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
-    const float2 krc = reinterpret_cast<const float2 *>(kc_row)[lane & 15];
-    const float2 krs = reinterpret_cast<const float2 *>(ks_row)[lane & 15];
-    Rope32 rope_row;
-    if (rope_on)
-        load_rope32_uniform(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2),
-                            a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), rope_row);
+    int64_t pn = -1;                                   // the new key's slot (uniform; none unfused)
     const float *sbase = a.k_scale + (int64_t)b * a.cache_seq_stride;
     float ks_u;                                        // key scale of this lane's key in the current unit
-    {
+    if constexpr (kFused) {
+        pn = L - 1 < blk0 + span ? L - 1 : -1;
+        const uint4 *qs = reinterpret_cast<const uint4 *>(a.q_bf16 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
+        const uint4 qp0 = qs[0], qp1 = qs[1];
+        const float wr = a.w[(int64_t)qrow * LK_HEADS + head];
+        const uint32_t kn = reinterpret_cast<const uint32_t *>(a.k_new + (int64_t)b * LK_DIM)[lane];
+        const float *kc_row = rope_on ? a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
+        const float *ks_row = rope_on ? a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2) : reinterpret_cast<const float *>(a.k_new);
+        const float2 krc = reinterpret_cast<const float2 *>(kc_row)[lane & 15];
+        const float2 krs = reinterpret_cast<const float2 *>(ks_row)[lane & 15];
+        Rope32 rope_row;
+        if (rope_on)
+            load_rope32_uniform(a.rope_cos + (int64_t)qrow * (LK_ROPE_DIM / 2),
+                                a.rope_sin + (int64_t)qrow * (LK_ROPE_DIM / 2), rope_row);
+        {
+            const int64_t s = blk0 + 64 * wave + lane;
+            ks_u = sbase[s < L ? s : 0];
+        }
+        {
+            uint32_t in[8] = {qp0.x, qp0.y, qp0.z, qp0.w, qp1.x, qp1.y, qp1.z, qp1.w};
+            if (rope_on) {
+                Rope16 rope;
+                pick_rope16(rope_row, sub, rope);
+                rope_row16(in, rope, sub);
+            }
+            uint32_t codes[4];
+            int j;
+            quantize_row16(in, codes, j);
+            const uint4 piece = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+            *reinterpret_cast<uint4 *>(sq + head * kQPitch + 16 * sub) = piece;
+            const float we = fold_weight(wr, j);
+            if (sub == 0) sw[head] = we;
+            if (blk0 == 0 && a.q_fp8_out) {
+                *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) = piece;
+                if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = we;
+            }
+        }
+        if (pn >= 0 && wave == 0) {                        // the new key, spread over wave 0 (2 features a lane)
+            uint32_t kin = kn;
+            if (rope_on) rope_row_wave(kin, krc, krs);
+            int kj;
+            const uint32_t kc = quantize_row_wave(kin, kj);
+            const int64_t row_off = (int64_t)b * a.cache_seq_stride + pn;
+            reinterpret_cast<uint16_t *>(a.k_cache + row_off * LK_DIM)[lane] = (uint16_t)kc;
+            reinterpret_cast<uint16_t *>(snew)[lane] = (uint16_t)kc;
+            if (lane == 0) {
+                const float ksc = __builtin_ldexpf(1.0f, kj);
+                a.k_scale[row_off] = ksc;
+                sm.d.snew_scale = ksc;
+            }
+        }
+    } else {                                           // lk_index_score: the prepared query
+        const uint4 piece =
+            *reinterpret_cast<const uint4 *>(a.q_fp8 + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub);
+        const float we = a.w_eff[(int64_t)qrow * LK_HEADS + head];
         const int64_t s = blk0 + 64 * wave + lane;
         ks_u = sbase[s < L ? s : 0];
-    }
-    {
-        uint32_t in[8] = {qp0.x, qp0.y, qp0.z, qp0.w, qp1.x, qp1.y, qp1.z, qp1.w};
-        if (rope_on) {
-            Rope16 rope;
-            pick_rope16(rope_row, sub, rope);
-            rope_row16(in, rope, sub);
-        }
-        uint32_t codes[4];
-        int j;
-        quantize_row16(in, codes, j);
-        const uint4 piece = make_uint4(codes[0], codes[1], codes[2], codes[3]);
         *reinterpret_cast<uint4 *>(sq + head * kQPitch + 16 * sub) = piece;
-        const float we = fold_weight(wr, j);
         if (sub == 0) sw[head] = we;
-        if (blk0 == 0 && a.q_fp8_out) {
-            *reinterpret_cast<uint4 *>(a.q_fp8_out + ((int64_t)qrow * LK_HEADS + head) * LK_DIM + 16 * sub) = piece;
-            if (sub == 0) a.w_eff_out[(int64_t)qrow * LK_HEADS + head] = we;
-        }
-    }
-    if (pn >= 0 && wave == 0) {                        // the new key, spread over wave 0 (2 features a lane)
-        uint32_t kin = kn;
-        if (rope_on) rope_row_wave(kin, krc, krs);
-        int kj;
-        const uint32_t kc = quantize_row_wave(kin, kj);
-        const int64_t row_off = (int64_t)b * a.cache_seq_stride + pn;
-        reinterpret_cast<uint16_t *>(a.k_cache + row_off * LK_DIM)[lane] = (uint16_t)kc;
-        reinterpret_cast<uint16_t *>(snew)[lane] = (uint16_t)kc;
-        if (lane == 0) {
-            const float ksc = __builtin_ldexpf(1.0f, kj);
-            a.k_scale[row_off] = ksc;
-            sm.d.snew_scale = ksc;
-        }
     }
     __syncthreads();                                   // query prepared, phase 0 landed
     QueryRaw raw;
@@ -901,7 +826,7 @@ constexpr int kPipeWaves = 4;
 constexpr int kPipeThreads = 64 * kPipeWaves;
 constexpr int kPipeTiles = 8;
 constexpr int kPipeFly = 4;
-static_assert(kPipeWaves * kPipeTiles * 32 == kDecKeysPerBlock, "the same key blocks as decode_item");
+static_assert(kPipeWaves * kPipeTiles * 32 == kDecKeysPerBlock, "1024-key blocks, as the other decode kernels");
 static_assert(LK_HEADS * LK_DIM / 16 == 2 * kPipeThreads, "two 16-byte query pieces per thread");
 
 __global__ void __launch_bounds__(kPipeThreads) decode_pipe_kernel(DecodeArgs a) {
@@ -962,74 +887,6 @@ __global__ void __launch_bounds__(kPipeThreads) decode_pipe_kernel(DecodeArgs a)
     QueryFrag f;
     convert_query(raw, f);
     pipelined_tiles<kPipeTiles, kPipeFly>(kv, load_tile, f, ks, key0, T, L, out);
-}
-
-// lk_index_score over more items than the chip runs at once (many rows, or ragged rows
-// whose key blocks mostly end early): a block per compute unit walks a contiguous range
-// of the valid items, in row order, so it stages each row's query once for all of its
-// items of that row, and items of different lengths even out across blocks.  Every
-// block derives the same schedule from the row lengths: row r has
-// ceil(L_r / kDecKeysPerBlock) items, and the key blocks past them are swept to -inf by
-// block r % grid.
-constexpr int kPersistMaxRows = kDecThreads;
-__global__ void __launch_bounds__(kDecThreads) decode_persistent_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) DecodeShared sm;
-    __shared__ int32_t first_item[kPersistMaxRows + 1];   // row r's items: first_item[r] .. first_item[r+1]-1
-    __shared__ int32_t wave_tot[kDecWaves];
-    LK_POISON_LDS_OBJS(sm, first_item, wave_tot);
-    const int nrows = a.rows.B * a.rows.S;             // <= kPersistMaxRows (host check)
-    const int64_t T = a.rows.T;
-    const int tid = threadIdx.x, lane = __lane_id(), wave = tid >> 6;
-    int nv = 0;
-    if (tid < nrows) {
-        const int64_t L = row_len(a.rows, tid / a.rows.S, tid % a.rows.S);
-        nv = (int)((L + kDecKeysPerBlock - 1) / kDecKeysPerBlock);
-    }
-    // exclusive scan of nv over the rows (one per thread)
-    int incl = nv;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += y;
-    }
-    if (lane == 63) wave_tot[wave] = incl;
-    __syncthreads();
-    int base = 0;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; w++) base += w < wave ? wave_tot[w] : 0;
-    first_item[tid] = base + incl - nv;
-    if (tid == kDecThreads - 1) first_item[kDecThreads] = base + incl;
-    __syncthreads();
-    const int total = first_item[kDecThreads];
-    const int G = gridDim.x, g = blockIdx.x;
-    // -inf for the key blocks past each row's items
-    for (int r = g; r < nrows; r += G) {
-        const int64_t s0 = (int64_t)(first_item[r + 1] - first_item[r]) * kDecKeysPerBlock;
-        float *out = a.scores + (int64_t)r * T;
-        for (int64_t s = s0 + tid; s < T; s += kDecThreads) out[s] = -__builtin_inff();
-    }
-    const int i0 = (int)((int64_t)total * g / G), i1 = (int)((int64_t)total * (g + 1) / G);
-    int row = 0;
-    {                                                  // the row of item i0 (binary search)
-        int lo = 0, hi = nrows - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (first_item[mid] <= i0) lo = mid; else hi = mid - 1;
-        }
-        row = lo;
-    }
-    int prev = -1;
-    for (int it = i0; it < i1; it++) {
-        while (first_item[row + 1] <= it) row++;
-        // row and the item's first key are the same in every lane (LDS reads at a
-        // uniform address); saying so keeps the row's addresses, and the RoPE table row
-        // loaded through them, in scalar registers.
-        row = __builtin_amdgcn_readfirstlane(row);
-        const int item0 = __builtin_amdgcn_readfirstlane(first_item[row]);
-        const int64_t blk0 = (int64_t)(it - item0) * kDecKeysPerBlock;
-        decode_item(a, sm, row, blk0, row != prev, it == i0);
-        prev = row;
-    }
 }
 
 // ------------------------------------------------------------------ prefill (S > 1)
@@ -1304,22 +1161,17 @@ int cu_count() {
 }
 
 // Decode grid (S == 1): one block per (row, key block) when that fits the chip about
-// once; beyond, the persistent form with one block per compute unit.
+// once; beyond, balanced runs of 512-key units, one block per compute unit (or per row
+// when the rows outnumber them).
 template <bool kFused>
 hipError_t launch_decode_grid(const DecodeArgs &a, hipStream_t stream) {
     const RowsDev &rows = a.rows;
     const int64_t nblk = (rows.T + kDecKeysPerBlock - 1) / kDecKeysPerBlock;
     const int64_t nrows = (int64_t)rows.B * rows.S;
     const int cus = cu_count();
-    if (nrows <= kPersistMaxRows && nblk * nrows * 4 > (int64_t)cus * 5) {
-        if constexpr (kFused) {                        // S == 1: runs of 512-key units, one per block
-            static_assert(kUnitMaxRows >= kPersistMaxRows, "the unit schedule takes every such row");
-            const unsigned grid = (unsigned)(nrows > cus ? nrows : cus);
-            return launch(decode_units_kernel, dim3(grid), dim3(kDmaThreads), 0u, stream, a);
-        } else {
-            const unsigned grid = (unsigned)(nblk * nrows < cus ? nblk * nrows : cus);
-            return launch(decode_persistent_kernel, dim3(grid), dim3(kDecThreads), 0u, stream, a);
-        }
+    if (nrows <= kUnitMaxRows && nblk * nrows * 4 > (int64_t)cus * 5) {
+        const unsigned grid = (unsigned)(nrows > cus ? nrows : cus);   // S == 1: runs of 512-key units
+        return launch(decode_units_kernel<kFused>, dim3(grid), dim3(kDmaThreads), 0u, stream, a);
     }
     dim3 grid((unsigned)nblk, (unsigned)rows.B);
     if constexpr (kFused) return launch(decode_kernel<false>, grid, dim3(kDmaThreads), 0u, stream, a);

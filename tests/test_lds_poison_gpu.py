@@ -8,8 +8,8 @@ scores, top-k indices, written cache rows, quantized queries, folded weights, an
 sparse MLA output.  The workloads reach each kernel: the fused decode step
 (decode_kernel), its ragged many-row form (decode_units_kernel), the one-launch select
 (decode_kernel with the top-k in LDS), the separate score calls (decode_pipe_kernel,
-decode_persistent_kernel), prefill with both grid forms (score_prefill_kernel), both
-top-k block shapes, and the sparse MLA split kernel."""
+and the unit runs on a prepared query), prefill with both grid forms
+(score_prefill_kernel), both top-k block shapes, and the sparse MLA split kernel."""
 import contextlib
 import os
 
@@ -85,8 +85,8 @@ def test_fused_decode_and_select(poisoned):
 
 
 def test_ragged_many_rows(poisoned):
-    """64 ragged rows: the fused step's unit runs (decode_units_kernel), the separate
-    score's persistent schedule (decode_persistent_kernel), topk_kernel<1024>."""
+    """64 ragged rows: the unit runs (decode_units_kernel) of the fused step and of the
+    separate score on a prepared query, topk_kernel<1024>."""
     inp = W.make_inputs(W.WORKLOADS["ragged_decode_b64"], seed=0)
     log("[poison] ragged_decode_b64 fused step")
     _compare(*_both(poisoned, lambda: gpu_pipeline_fused(inp)))
